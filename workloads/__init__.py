@@ -1,0 +1,110 @@
+"""Seeded synthetic workloads for the packed text/video/stereo-audio attention path.
+
+This module is shared by the oracle side and the HIP side and holds none of the
+method's arithmetic: it only names the segment tables (which segments, in which
+row order, with their sizes and time origins) and draws the seeded Q, K, V
+inputs.  Everything that turns a segment table into coordinates, rotates, or
+attends lives elsewhere, twice, independently.
+
+Segment tables follow the packed-sequence description of the pages:
+"Inside MiniMax H3: One DiT Stream for Text, Video, and Stereo Audio" (section 2:
+every modality enters one packed sequence; section 4: the shared physical
+timeline) and "MiniMax H3 - one transformer that denoises video and audio
+together" (latent-frame paragraph: a 44x80 latent sheet patchified 1x2x2 is
+22x40 = 880 tokens; 31 latent frames give 27,280 video tokens).
+
+Times are integers in thirds of one audio latent (1/120 s), so that the video
+advance of 20/3 clock units per latent frame is exact.
+"""
+from collections import namedtuple
+
+import numpy as np
+
+TEXT, VIDEO, AUDIO = 0, 1, 2
+
+# kind   : TEXT / VIDEO / AUDIO
+# frames : TEXT: tokens | VIDEO: latent frames (1 = a still / reference image) | AUDIO: 40 Hz steps
+# grid_h : VIDEO: patch rows | TEXT, AUDIO: 1
+# grid_w : VIDEO: patch columns | AUDIO: channels (2 = stereo) | TEXT: 1
+# t0_thirds, dt_thirds : time of the first frame and advance per frame, in thirds of a clock unit
+Segment = namedtuple("Segment", "kind frames grid_h grid_w t0_thirds dt_thirds")
+
+
+def text(n, t0):
+    """n text tokens at integer clock positions t0, t0+1, ..."""
+    return Segment(TEXT, n, 1, 1, 3 * t0, 3)
+
+
+def video(frames, gh, gw, t0_thirds=0):
+    """Latent frames of gh x gw patches, 20/3 clock units apart (4 source frames at 24 fps on a 40 Hz clock)."""
+    return Segment(VIDEO, frames, gh, gw, t0_thirds, 20)
+
+
+def audio(steps, t0, channels=2):
+    """40 Hz audio latents, one token per channel per step, one clock unit apart."""
+    return Segment(AUDIO, steps, 1, channels, 3 * t0, 3)
+
+
+def _ref2va():
+    segs = [text(1024, -1684)]
+    # nine reference images, one latent slot each, back to back, the last ending at -20/3
+    segs += [video(1, 22, 40, t0_thirds=-180 + 20 * m) for m in range(9)]
+    # three reference audio clips of 200 steps x 2 channels, back to back before the images
+    segs += [audio(200, -660 + 200 * a) for a in range(3)]
+    segs += [video(31, 22, 40), audio(200, 0)]
+    return segs
+
+
+# name -> (n_heads, segment table); row order is the table order
+CONFIGS = {
+    "tiny": (2, [text(16, -16), video(1, 4, 8), audio(8, 0)]),
+    "4s": (42, [text(256, -256), video(25, 22, 40), audio(160, 0)]),
+    "5s": (42, [text(512, -512), video(31, 22, 40), audio(200, 0)]),
+    "ref2va": (42, _ref2va()),
+    "15s": (42, [text(512, -512), video(91, 22, 40), audio(600, 0)]),
+}
+
+# expected packed lengths stated with each workload
+CONFIG_TOKENS = {"tiny": 64, "4s": 22576, "5s": 28192, "ref2va": 37824, "15s": 81792}
+
+HEAD_DIM = 128
+ROPE_SECTIONS = (32, 48, 48)
+ROPE_THETAS = (10000.0, 10000.0, 10000.0)
+DEFAULT_SEED = 20260731
+
+
+def n_tokens(segments):
+    """Row count of a segment table (sizes only, no coordinates)."""
+    n = 0
+    for s in segments:
+        n += s.frames * s.grid_h * s.grid_w
+    return n
+
+
+def f32_to_bf16_bits(x):
+    """Round float32 values to bfloat16 (round to nearest, ties to even) and return the raw uint16 bits."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (b >> np.uint32(16)) & np.uint32(1)
+    return ((b + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits):
+    """Widen raw bfloat16 bits to float32 (exact)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def normal_bf16(shape, seed, scale=1.0):
+    """Seeded N(0, scale^2) draws rounded to bfloat16; returns uint16 bits."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal(shape, dtype=np.float32)
+    if scale != 1.0:
+        x *= np.float32(scale)
+    return f32_to_bf16_bits(x)
+
+
+def qkv(n, h, seed=DEFAULT_SEED, d=HEAD_DIM, q_scale=1.0):
+    """Q, K, V as bf16 bit arrays [n, h, d]; seeds seed, seed+1, seed+2."""
+    q = normal_bf16((n, h, d), seed, q_scale)
+    k = normal_bf16((n, h, d), seed + 1)
+    v = normal_bf16((n, h, d), seed + 2)
+    return q, k, v
