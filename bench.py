@@ -1,0 +1,145 @@
+"""Benchmark of the MM-RoPE + full-attention hot path on one MI355X.
+
+One step = one pass of the whole path over the 5 s 704x1280 packed sequence
+(512 text + 31 x 22 x 40 video + 200 x 2 audio = 28,192 rows, 42 heads x 128):
+  h3attn_rope_qk   rotate K by its (t, h, w) coordinates (HBM-bound pass)
+  h3attn_forward   rotate Q in the tile load, then softmax(Q~ K~^T / sqrt(128)) V
+Inputs are seeded synthetic bf16 N(0, 1) tensors, resident in HBM before the
+timed region.  Prints one JSON line.
+
+FLOP counted per step: 4 N^2 H D (the two products of full attention).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads as W  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+METRIC = "MM-RoPE+attention TFLOP/s & % bf16 MFMA peak, 28,192-token packed seq"
+WORKLOAD = ("5 s 704x1280 packed sequence: 512 text + 31 latent frames x 22x40 video + "
+            "200 steps x 2 audio = 28,192 tokens; 42 heads x 128; RoPE t/h/w 32/48/48, base 1e4")
+
+
+def cpu_baseline(name, q, k, v, segs, budget_s):
+    """Time the fp64 oracle on a bounded sample: head 0, query rows in blocks of 256, ~budget_s."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = 1
+    n = q.shape[0]
+    c = oracle.build_coords(segs)
+    qh = oracle.bf16_bits_to_f64(q[:, :1])
+    kh = oracle.bf16_bits_to_f64(k[:, :1])
+    vh = oracle.bf16_bits_to_f64(v[:, :1])
+    rows_done, t_used = 0, 0.0
+    block = 256
+    while t_used < budget_s and rows_done < n:
+        rows = np.arange(rows_done, min(n, rows_done + block))
+        t0 = time.perf_counter()
+        oracle.attention(qh, kh, vh, c, W.ROPE_SECTIONS, W.ROPE_THETAS, rows=rows, block=block)
+        t_used += time.perf_counter() - t0
+        rows_done += len(rows)
+    flops = 4.0 * rows_done * n * W.HEAD_DIM
+    return {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": "%s workload, head 0 of 42, query rows 0..%d against all %d keys (RoPE included), "
+                      "%.1f s of fp64 numpy; FLOP 4*rows*N*D" % (name, rows_done - 1, n, t_used)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="5s", choices=list(W.CONFIGS))
+    ap.add_argument("--mode", default="fused", choices=["fused", "prerotated"])
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the path is single-GPU (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import stream_audio_video_amd as h3
+    h3.load_library()
+    dev = torch.device("cuda:0")
+    h, segs = W.CONFIGS[args.config]
+    n = W.n_tokens(segs)
+    D = W.HEAD_DIM
+    q, k, v = W.qkv(n, h, W.DEFAULT_SEED)
+    to_dev = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    coords = torch.from_numpy(h3.build_coords(segs)).to(dev)
+    cfg = h3.rope_cfg(W.ROPE_SECTIONS, W.ROPE_THETAS)
+    stride = qd.stride(0)
+    krot = torch.empty_like(kd)
+    qrot = torch.empty_like(qd) if args.mode == "prerotated" else None
+    o = torch.empty_like(qd)
+    lse = torch.empty((h, n), dtype=torch.float32, device=dev)
+    fused = args.mode == "fused"
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        if fused:
+            h3.rope_qk(cfg, coords, None, None, kd, krot, n, h, stride)
+        else:
+            h3.rope_qk(cfg, coords, qd, qrot, kd, krot, n, h, stride)
+        if ev is not None:
+            ev[1].record()
+        h3.forward(cfg, coords, 1 if fused else 0, qd if fused else qrot, krot, vd, o, lse, n, h, stride,
+                   stride)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    rope_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    flop = 4.0 * n * n * h * D
+    value = flop / (ms_step * 1e-3) / 1e12
+    achieved = flop / (attn_ms * 1e-3) / 1e12
+    rope_bytes = (2 if fused else 4) * n * h * D * 2 + 12 * n
+
+    cpu = None
+    if args.cpu_budget > 0:
+        cpu = cpu_baseline(args.config, q, k, v, segs, args.cpu_budget)
+
+    rec = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD if args.config == "5s" else args.config, "n_tokens": n, "heads": h,
+                   "head_dim": D, "rope_sections": list(W.ROPE_SECTIONS), "mode": args.mode,
+                   "frac_of_peak_step": round(value / PEAK_BF16_TFLOPS, 4),
+                   "tokens_per_s": round(n / (ms_step * 1e-3), 1),
+                   "rope_ms": round(rope_ms, 4), "rope_GBps": round(rope_bytes / (rope_ms * 1e-3) / 1e9, 1),
+                   "attn_ms": round(attn_ms, 4)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

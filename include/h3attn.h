@@ -1,0 +1,156 @@
+/*
+ * h3attn.h - C ABI of the MI355X (gfx950) library for MM-RoPE + full
+ * bidirectional attention over one packed text / video / stereo-audio sequence.
+ *
+ * The operation is the attention of the single-stream Omni-Transformer
+ * described in "Inside MiniMax H3: One DiT Stream for Text, Video, and Stereo
+ * Audio" (section 2: text, reference media, noisy video latents and noisy audio
+ * latents share one attention sequence; section 4: RoPE coordinates on a shared
+ * physical timeline; section 6: full attention) and in "MiniMax H3 - one
+ * transformer that denoises video and audio together" (latent frames and the
+ * 1x2x2 patch grid, the 40 Hz clock and the 5/3 frame rescale, text as 1-D RoPE,
+ * position_ids -> rope() -> rotate Q and K, the normalised spatial grid).
+ *
+ * Conventions for every call:
+ *  - All buffers are owned by the caller.  The library allocates no device
+ *    memory and keeps no state beyond a per-device cache of device properties.
+ *  - Device calls are asynchronous on `stream` (a hipStream_t passed as void*;
+ *    NULL is the default stream) and never synchronise.
+ *  - Arguments are validated before any write or launch: on error nothing has
+ *    been written and nothing has been launched.
+ *  - Return value: H3ATTN_OK (0) or one of the negative codes below.  No C++
+ *    exception crosses this boundary.  The calls are thread-safe.
+ *  - Q, K, V, O tensors are bfloat16, row-major [n_tokens][n_heads][head_dim]
+ *    with a row stride given in elements (>= n_heads * head_dim, a multiple of
+ *    8), base pointers 16-byte aligned.  head_dim must be 128.
+ */
+#ifndef H3ATTN_H
+#define H3ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  H3ATTN_OK = 0,
+  H3ATTN_EINVAL = -1,       /* null pointer, bad size, bad config, misalignment */
+  H3ATTN_ERANGE = -2,       /* capacity too small; coordinate or size out of exact range */
+  H3ATTN_EUNSUPPORTED = -3, /* current device is not gfx950 */
+  H3ATTN_EHIP = -4          /* HIP runtime or launch error */
+};
+
+/* Segment kinds of the packed sequence. */
+enum { H3_SEG_TEXT = 0, H3_SEG_VIDEO = 1, H3_SEG_AUDIO = 2 };
+
+/*
+ * One segment of the packed sequence.  Times are integers in thirds of one
+ * clock unit (one audio latent, 1/40 s), so that the video advance of
+ * 4 source frames x 5/3 = 20/3 units per latent frame is exact.
+ *
+ *   kind      H3_SEG_TEXT | H3_SEG_VIDEO | H3_SEG_AUDIO
+ *   frames    TEXT: tokens | VIDEO: latent frames (1 = still or reference image)
+ *             | AUDIO: 40 Hz steps.  0 is allowed (no rows).
+ *   grid_h    VIDEO: patch rows (22 for a 44x80 latent sheet) | TEXT, AUDIO: 1
+ *   grid_w    VIDEO: patch columns (40) | AUDIO: channels (2) | TEXT: 1
+ *   t0_thirds time of the first frame / token / step, in thirds
+ *   dt_thirds advance per frame: VIDEO 20, AUDIO 3, TEXT 3 (any value allowed)
+ */
+typedef struct {
+  int32_t kind;
+  int32_t frames;
+  int32_t grid_h;
+  int32_t grid_w;
+  int32_t t0_thirds;
+  int32_t dt_thirds;
+} h3attn_segment;
+
+/*
+ * Rotary configuration: head_dim (must be 128) is split into three contiguous
+ * sections for the t, h and w axes (sec[0] + sec[1] + sec[2] == head_dim, each
+ * even and >= 0).  Inside section a, pair p rotates dims (o_a + 2p, o_a + 2p + 1)
+ * by pos_a * theta[a]^(-2p / sec[a]); theta[a] > 0.  The inverse frequencies
+ * are computed, not loaded ("MiniMax H3 - one transformer that denoises video
+ * and audio together", inv_freq paragraph).  The workloads here use
+ * {128, {32, 48, 48}, {1e4, 1e4, 1e4}}.
+ */
+typedef struct {
+  int32_t head_dim;
+  int32_t sec[3];
+  double theta[3];
+} h3attn_rope_cfg;
+
+/*
+ * Host call.  Builds the (t, h, w) coordinate of every packed row.
+ *   Rows follow the segment order.  VIDEO rows are frame-major, then row-major
+ *   (r, c); AUDIO rows step-major, channel-minor; TEXT rows in order.
+ *   t = RN32(t3 / 3) with t3 = t0_thirds + f * dt_thirds (exact, round to
+ *   nearest even).  TEXT: h = w = 0.  AUDIO: h = 0, w = channel (left and right
+ *   share t: section 4 of the thread).  VIDEO: the patch grid normalised by
+ *   sqrt(grid_h * grid_w) and centred on the [0, 32) canvas with the aspect kept:
+ *   s = 16 / sqrt(gh * gw); h_r = RN32(16 + (2r + 1 - gh) * s),
+ *   w_c = RN32(16 + (2c + 1 - gw) * s), evaluated in binary64 without fusion.
+ * Arguments:
+ *   segs, n_segs     segment table (n_segs >= 0; segs may be NULL iff n_segs == 0)
+ *   coords           host float32 [capacity_rows][3], or NULL to only count
+ *   capacity_rows    rows available in coords
+ *   n_tokens         out: number of rows (always written on success)
+ * Errors: EINVAL (bad kind or sizes, null n_tokens), ERANGE (|t3| >= 2^24,
+ *   rows >= 2^31, or capacity too small; *n_tokens still holds the count when
+ *   only the capacity is short).
+ */
+int h3attn_build_coords(const h3attn_segment* segs, int32_t n_segs, float* coords,
+                        int64_t capacity_rows, int64_t* n_tokens);
+
+/*
+ * Device call.  Rotates Q and/or K by the rows' coordinates (the rope() step of
+ * the position chain; V is never rotated).  Out-of-place, or in place when
+ * the output pointer equals the input pointer.  The cos/sin of each
+ * (row, pair) angle are formed once per row from a binary64 angle and reused
+ * over all heads; the rotation runs in float32 and rounds to bfloat16 (nearest
+ * even).
+ *   cfg            rotary configuration (host pointer)
+ *   coords_dev     device float32 [n_tokens][3]
+ *   q_in, q_out    bf16 [n_tokens][n_heads][128]; both NULL to skip Q
+ *   k_in, k_out    same for K; both NULL to skip K
+ *   row_stride     elements between rows, for all four tensors
+ * n_tokens == 0 is a no-op.  Errors: EINVAL, ERANGE (n_tokens * row_stride
+ *   >= 2^31), EUNSUPPORTED, EHIP.
+ */
+int h3attn_rope_qk(const h3attn_rope_cfg* cfg, const float* coords_dev,
+                   const void* q_in, void* q_out, const void* k_in, void* k_out,
+                   int64_t n_tokens, int32_t n_heads, int64_t row_stride, void* stream);
+
+/*
+ * Device call.  Per head, O = softmax(Q~ K^T * scale) V over all n_tokens rows:
+ * full bidirectional attention with no mask (section 6 of the thread; the open
+ * release runs full attention).  K must already be rotated (h3attn_rope_qk with
+ * q = NULL).  Q is rotated inside the kernel's Q-tile load when rope_q != 0
+ * (same rounding as h3attn_rope_qk, so both routes give identical bits), or used
+ * as given when rope_q == 0 (already rotated).
+ *   cfg, coords_dev   as above (coords_dev may be NULL when rope_q == 0)
+ *   q, k, v           bf16 [n_tokens][n_heads][128], row stride row_stride_qkv
+ *   o                 out: bf16 [n_tokens][n_heads][128], row stride row_stride_o
+ *   lse               out (optional, may be NULL): float32 [n_heads][n_tokens],
+ *                     natural log of sum_j exp(scale * q~.k_j)
+ *   scale             softmax scale; <= 0 selects 1/sqrt(128)
+ * o must not alias q, k or v.  n_tokens == 0 is a no-op.  Errors: EINVAL,
+ *   ERANGE, EUNSUPPORTED, EHIP.
+ */
+int h3attn_forward(const h3attn_rope_cfg* cfg, const float* coords_dev, int32_t rope_q,
+                   const void* q, const void* k, const void* v, void* o, float* lse,
+                   int64_t n_tokens, int32_t n_heads, int64_t row_stride_qkv,
+                   int64_t row_stride_o, float scale, void* stream);
+
+/* Static description of an error code (never NULL). */
+const char* h3attn_strerror(int code);
+
+/* Library version string, e.g. "h3attn 0.1.0 gfx950". */
+const char* h3attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* H3ATTN_H */

@@ -1,0 +1,153 @@
+// C ABI of the library: argument validation, device check and dispatch to the
+// kernel launchers.  Every check runs before any launch, so an error leaves
+// all outputs untouched.
+#include <atomic>
+#include <cmath>
+#include <cstring>
+
+#include "h3attn.h"
+#include "launch.hpp"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// 0 = unknown, 1 = gfx950, 2 = other
+std::atomic<int> g_device_kind[kMaxDevices];
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return H3ATTN_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return H3ATTN_EUNSUPPORTED;
+  int kind = g_device_kind[dev].load(std::memory_order_relaxed);
+  if (kind == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return H3ATTN_EHIP;
+    kind = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_device_kind[dev].store(kind, std::memory_order_relaxed);
+  }
+  return kind == 1 ? H3ATTN_OK : H3ATTN_EUNSUPPORTED;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int make_table(const h3attn_rope_cfg* cfg, h3::RopeTable* tab) {
+  if (cfg == nullptr || cfg->head_dim != h3::kHeadDim) return H3ATTN_EINVAL;
+  int sum = 0;
+  for (int a = 0; a < 3; ++a) {
+    if (cfg->sec[a] < 0 || (cfg->sec[a] & 1)) return H3ATTN_EINVAL;
+    if (!(cfg->theta[a] > 0.0) || !std::isfinite(cfg->theta[a])) return H3ATTN_EINVAL;
+    sum += cfg->sec[a];
+  }
+  if (sum != h3::kHeadDim) return H3ATTN_EINVAL;
+  int pair = 0;
+  for (int a = 0; a < 3; ++a) {
+    const int d = cfg->sec[a];
+    for (int p = 0; p < d / 2; ++p)
+      tab->freq[pair++] = std::pow(cfg->theta[a], -(2.0 * p) / static_cast<double>(d));
+  }
+  tab->b1 = cfg->sec[0] / 2;
+  tab->b2 = (cfg->sec[0] + cfg->sec[1]) / 2;
+  return H3ATTN_OK;
+}
+
+int check_tensor_geometry(int64_t n_tokens, int32_t n_heads, int64_t stride) {
+  if (n_tokens < 0 || n_heads <= 0) return H3ATTN_EINVAL;
+  if (stride < int64_t(n_heads) * h3::kHeadDim || (stride & 7) != 0) return H3ATTN_EINVAL;
+  // element offsets are 32-bit inside the kernels
+  if (n_tokens > 0 && n_tokens * stride >= (int64_t(1) << 31)) return H3ATTN_ERANGE;
+  return H3ATTN_OK;
+}
+
+bool overlaps(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + uintptr_t(b_bytes) && b0 < a0 + uintptr_t(a_bytes);
+}
+
+}  // namespace
+
+extern "C" int h3attn_rope_qk(const h3attn_rope_cfg* cfg, const float* coords_dev,
+                              const void* q_in, void* q_out, const void* k_in, void* k_out,
+                              int64_t n_tokens, int32_t n_heads, int64_t row_stride,
+                              void* stream) {
+  h3::RopeArgs a;
+  int rc = make_table(cfg, &a.tab);
+  if (rc != H3ATTN_OK) return rc;
+  if ((q_in == nullptr) != (q_out == nullptr) || (k_in == nullptr) != (k_out == nullptr))
+    return H3ATTN_EINVAL;
+  if (q_in == nullptr && k_in == nullptr) return H3ATTN_EINVAL;
+  for (const void* p : {q_in, static_cast<const void*>(q_out), k_in, static_cast<const void*>(k_out)})
+    if (p != nullptr && !aligned16(p)) return H3ATTN_EINVAL;
+  rc = check_tensor_geometry(n_tokens, n_heads, row_stride);
+  if (rc != H3ATTN_OK) return rc;
+  if (n_tokens == 0) return H3ATTN_OK;
+  if (coords_dev == nullptr) return H3ATTN_EINVAL;
+  rc = check_device();
+  if (rc != H3ATTN_OK) return rc;
+  a.coords = coords_dev;
+  a.q_in = static_cast<const uint16_t*>(q_in);
+  a.q_out = static_cast<uint16_t*>(q_out);
+  a.k_in = static_cast<const uint16_t*>(k_in);
+  a.k_out = static_cast<uint16_t*>(k_out);
+  a.n = static_cast<int32_t>(n_tokens);
+  a.heads = n_heads;
+  a.stride = static_cast<int32_t>(row_stride);
+  return h3::launch_rope_qk(a, static_cast<hipStream_t>(stream)) == hipSuccess ? H3ATTN_OK
+                                                                               : H3ATTN_EHIP;
+}
+
+extern "C" int h3attn_forward(const h3attn_rope_cfg* cfg, const float* coords_dev, int32_t rope_q,
+                              const void* q, const void* k, const void* v, void* o, float* lse,
+                              int64_t n_tokens, int32_t n_heads, int64_t row_stride_qkv,
+                              int64_t row_stride_o, float scale, void* stream) {
+  h3::FwdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  int rc = make_table(cfg, &a.tab);
+  if (rc != H3ATTN_OK) return rc;
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return H3ATTN_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return H3ATTN_EINVAL;
+  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return H3ATTN_EINVAL;
+  if (!std::isfinite(scale)) return H3ATTN_EINVAL;
+  rc = check_tensor_geometry(n_tokens, n_heads, row_stride_qkv);
+  if (rc != H3ATTN_OK) return rc;
+  rc = check_tensor_geometry(n_tokens, n_heads, row_stride_o);
+  if (rc != H3ATTN_OK) return rc;
+  if (n_tokens > 0 && int64_t(n_heads) * n_tokens >= (int64_t(1) << 31)) return H3ATTN_ERANGE;
+  if (n_tokens == 0) return H3ATTN_OK;
+  if (rope_q && coords_dev == nullptr) return H3ATTN_EINVAL;
+  const int64_t in_bytes = ((n_tokens - 1) * row_stride_qkv + int64_t(n_heads) * h3::kHeadDim) * 2;
+  const int64_t out_bytes = ((n_tokens - 1) * row_stride_o + int64_t(n_heads) * h3::kHeadDim) * 2;
+  if (overlaps(o, out_bytes, q, in_bytes) || overlaps(o, out_bytes, k, in_bytes) ||
+      overlaps(o, out_bytes, v, in_bytes))
+    return H3ATTN_EINVAL;
+  rc = check_device();
+  if (rc != H3ATTN_OK) return rc;
+  if (scale <= 0.0f) scale = 1.0f / std::sqrt(static_cast<float>(h3::kHeadDim));
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.coords = coords_dev;
+  a.n = static_cast<int32_t>(n_tokens);
+  a.heads = n_heads;
+  a.stride_qkv = static_cast<int32_t>(row_stride_qkv);
+  a.stride_o = static_cast<int32_t>(row_stride_o);
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.rope_q = rope_q ? 1 : 0;
+  return h3::launch_attn_fwd(a, static_cast<hipStream_t>(stream)) == hipSuccess ? H3ATTN_OK
+                                                                                : H3ATTN_EHIP;
+}
+
+extern "C" const char* h3attn_strerror(int code) {
+  switch (code) {
+    case H3ATTN_OK: return "ok";
+    case H3ATTN_EINVAL: return "invalid argument";
+    case H3ATTN_ERANGE: return "size or coordinate out of range";
+    case H3ATTN_EUNSUPPORTED: return "device is not gfx950";
+    case H3ATTN_EHIP: return "HIP runtime error";
+    default: return "unknown error";
+  }
+}
+
+extern "C" const char* h3attn_version(void) { return "h3attn 0.1.0 gfx950"; }

@@ -1,0 +1,250 @@
+"""GPU parity of libh3attn against the fp64 oracle (MI355X, gfx950).
+
+Every call goes through the C ABI via the ctypes binding.  Inputs are the seeded
+bf16 workloads; expected values come from the oracle only.
+
+Tolerances.  Attention output: max |err| <= 2e-2 and RMS err <= 2e-3 (the
+stated acceptance bound), plus relative RMS <= 1e-2 and |LSE err| <= 1e-2.
+The LSE bound: the kernel multiplies bf16-rounded Q~ and K~, so each score
+s = q.k / sqrt(D) moves by about sqrt(2) * 2^-9 / sqrt(3) ~ 1.6e-3 (one std,
+unit-variance inputs); LSE is a weighted mean of score moves, and over all
+rows of a workload its worst case stays below ~5 std ~ 8e-3.
+RoPE pass: the kernel forms cos/sin from a binary64 angle and rotates in
+binary32, so before its final bf16 rounding it is within ~1e-6 of the pair
+norm of the exact value; after rounding each element is within half a bf16
+ulp of that, i.e. |gpu - exact| <= 0.5 ulp(|exact| + e) + e, e = 1e-6 * |pair|.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+SEC, TH = W.ROPE_SECTIONS, W.ROPE_THETAS
+MAX_ERR, RMS_ERR, REL_RMS, LSE_ERR = 2e-2, 2e-3, 1e-2, 1e-2
+
+_CACHE = {}
+
+
+def dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def host_bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def f64(bits):
+    return oracle.bf16_bits_to_f64(bits)
+
+
+def inputs(name, seed=W.DEFAULT_SEED, q_scale=1.0):
+    key = (name if isinstance(name, str) else repr(name), seed, q_scale)
+    if key not in _CACHE:
+        if len(_CACHE) > 2:
+            _CACHE.clear()
+        h, segs = W.CONFIGS[name] if isinstance(name, str) else name
+        n = W.n_tokens(segs)
+        q, k, v = W.qkv(n, h, seed, q_scale=q_scale)
+        _CACHE[key] = (h, segs, q, k, v)
+    return _CACHE[key]
+
+
+RAGGED = (3, [W.text(40, -40), W.video(2, 12, 20), W.audio(240, 0)])     # 1000 rows
+
+
+def run_gpu(h3, segs, q, k, v, fuse_q=True, scale=0.0):
+    coords = torch.from_numpy(h3.build_coords(segs)).cuda()
+    qd, kd, vd = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    o, lse = h3.mmrope_attention(qd, kd, vd, coords, scale=scale, fuse_q=fuse_q)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def check(o_gpu_bits, lse_gpu, o_ref, lse_ref, tag=""):
+    og = f64(o_gpu_bits)
+    err = og - o_ref
+    mx = float(np.max(np.abs(err)))
+    rms = float(np.sqrt(np.mean(err ** 2)))
+    rel = rms / float(np.sqrt(np.mean(o_ref ** 2)))
+    print("%s max|err| %.3e  rms %.3e  rel-rms %.3e" % (tag, mx, rms, rel), flush=True)
+    assert np.all(np.isfinite(og))
+    assert mx <= MAX_ERR and rms <= RMS_ERR and rel <= REL_RMS, (mx, rms, rel)
+    if lse_gpu is not None:
+        le = float(np.max(np.abs(lse_gpu - lse_ref)))
+        print("%s max|lse err| %.3e" % (tag, le), flush=True)
+        assert le <= LSE_ERR
+
+
+def bf16_ulp(x):
+    x = np.abs(x)
+    e = np.floor(np.log2(np.maximum(x, 2.0 ** -126)))
+    return 2.0 ** (e - 7)
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged", "5s"])
+def test_rope_kernel_matches_oracle(gpu_lib, name):
+    h3 = gpu_lib
+    h, segs, q, k, v = inputs(RAGGED if name == "ragged" else name)
+    n = W.n_tokens(segs)
+    coords_h = h3.build_coords(segs)
+    coords = torch.from_numpy(coords_h).cuda()
+    qd, kd = dev_bf16(q), dev_bf16(k)
+    qo, ko = torch.empty_like(qd), torch.empty_like(kd)
+    h3.rope_qk(h3.rope_cfg(), coords, qd, qo, kd, ko, n, h, qd.stride(0))
+    torch.cuda.synchronize()
+    rows = np.arange(n) if n <= 4096 else np.unique(np.r_[0, n - 1, np.random.default_rng(5).integers(0, n, 2000)])
+    for src, out in ((q, qo), (k, ko)):
+        x = f64(src[rows])
+        ref = oracle.rope(x, coords_h[rows], SEC, TH)
+        got = f64(host_bits(out)[rows])
+        pair = np.sqrt(x[..., 0::2] ** 2 + x[..., 1::2] ** 2).repeat(2, axis=-1)
+        e = 1e-6 * pair
+        tol = 0.5 * bf16_ulp(np.abs(ref) + e) + e
+        bad = np.abs(got - ref) > tol
+        assert not bad.any(), (int(bad.sum()), np.argwhere(bad)[:5])
+
+
+def test_rope_in_place_equals_out_of_place(gpu_lib):
+    h3 = gpu_lib
+    h, segs, q, k, v = inputs(RAGGED)
+    n = W.n_tokens(segs)
+    coords = torch.from_numpy(h3.build_coords(segs)).cuda()
+    kd = dev_bf16(k)
+    ko = torch.empty_like(kd)
+    h3.rope_qk(h3.rope_cfg(), coords, None, None, kd, ko, n, h, kd.stride(0))
+    h3.rope_qk(h3.rope_cfg(), coords, None, None, kd, kd, n, h, kd.stride(0))
+    torch.cuda.synchronize()
+    assert torch.equal(kd.view(torch.int16), ko.view(torch.int16))
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged"])
+def test_forward_full_matches_oracle(gpu_lib, name):
+    h3 = gpu_lib
+    h, segs, q, k, v = inputs(RAGGED if name == "ragged" else name)
+    o, lse = run_gpu(h3, segs, q, k, v)
+    c = oracle.build_coords(segs)
+    o_ref, lse_ref = oracle.attention(f64(q), f64(k), f64(v), c, SEC, TH)
+    check(host_bits(o), lse.cpu().numpy(), o_ref, lse_ref, name)
+
+
+@pytest.mark.parametrize("n", [1, 2, 31, 33, 63, 64, 65, 127, 128, 129, 255, 257])
+def test_forward_edge_lengths(gpu_lib, n):
+    h3 = gpu_lib
+    segs = [W.text(n, 0)]
+    q, k, v = W.qkv(n, 2, seed=100 + n)
+    o, lse = run_gpu(h3, segs, q, k, v)
+    o_ref, lse_ref = oracle.attention(f64(q), f64(k), f64(v), oracle.build_coords(segs), SEC, TH)
+    check(host_bits(o), lse.cpu().numpy(), o_ref, lse_ref, "n=%d" % n)
+
+
+def test_forward_fused_q_bitwise_equals_prerotated(gpu_lib):
+    h3 = gpu_lib
+    h, segs, q, k, v = inputs(RAGGED)
+    o1, l1 = run_gpu(h3, segs, q, k, v, fuse_q=True)
+    o2, l2 = run_gpu(h3, segs, q, k, v, fuse_q=False)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged"])
+def test_forward_peaky_softmax(gpu_lib, name):
+    """Q scaled by 8: sharp rows stress the online rescale."""
+    h3 = gpu_lib
+    h, segs, q, k, v = inputs(RAGGED if name == "ragged" else name, q_scale=8.0)
+    o, lse = run_gpu(h3, segs, q, k, v)
+    o_ref, lse_ref = oracle.attention(f64(q), f64(k), f64(v), oracle.build_coords(segs), SEC, TH)
+    og = f64(host_bits(o))
+    err = og - o_ref
+    mx, rms = float(np.max(np.abs(err))), float(np.sqrt(np.mean(err ** 2)))
+    rel = rms / float(np.sqrt(np.mean(o_ref ** 2)))
+    le = float(np.max(np.abs(lse.cpu().numpy() - lse_ref)))
+    print("peaky %s max %.3e rms %.3e rel %.3e lse %.3e" % (name, mx, rms, rel, le), flush=True)
+    # scores are 8x larger, so the bf16 rounding of Q~ and K~ moves them 8x more:
+    # about 8 * 2 * 2^-9 ~ 0.03 in the exponent; weights shift by ~3 % relative
+    assert mx <= 0.15 and rel <= 0.03 and le <= 0.05
+
+
+def test_forward_strided_views(gpu_lib):
+    """Q, K, V as views of one fused [N, 3, H, D] buffer; O with a padded row stride."""
+    h3 = gpu_lib
+    h, segs, q, k, v = inputs(RAGGED)
+    n = W.n_tokens(segs)
+    fused = torch.stack([dev_bf16(q), dev_bf16(k), dev_bf16(v)], dim=1).contiguous()   # [N, 3, H, D]
+    qv, kv, vv = fused[:, 0], fused[:, 1], fused[:, 2]
+    coords = torch.from_numpy(h3.build_coords(segs)).cuda()
+    kr = torch.empty_like(fused)[:, 1]
+    cfg = h3.rope_cfg()
+    h3.rope_qk(cfg, coords, None, None, kv, kr, n, h, fused.stride(0))
+    vv2 = torch.empty_like(fused)
+    vv2[:, 2] = vv
+    obuf = torch.zeros((n, h * 128 + 64), dtype=torch.bfloat16, device="cuda")
+    h3.forward(cfg, coords, 1, qv, kr, vv2[:, 2], obuf, None, n, h, fused.stride(0), obuf.stride(0))
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention(f64(q), f64(k), f64(v), oracle.build_coords(segs), SEC, TH)
+    check(host_bits(obuf[:, :h * 128].contiguous()).reshape(n, h, 128), None, o_ref, lse_ref, "strided")
+    assert torch.all(obuf[:, h * 128:] == 0)       # padding untouched
+
+
+def test_forward_closed_forms(gpu_lib):
+    h3 = gpu_lib
+    h, segs, q, k, v = inputs(RAGGED)
+    n = W.n_tokens(segs)
+    # all V rows equal -> O = that row (to bf16 rounding)
+    vc = np.broadcast_to(v[:1], v.shape).copy()
+    o, _ = run_gpu(h3, segs, q, k, vc)
+    assert np.max(np.abs(f64(host_bits(o)) - f64(vc))) <= 2.0 ** -8 * np.max(np.abs(f64(vc)))
+    # Q = 0 -> O = mean of V, LSE = log N
+    o, lse = run_gpu(h3, segs, np.zeros_like(q), k, v)
+    mean = f64(v).mean(0, keepdims=True)
+    assert np.max(np.abs(f64(host_bits(o)) - mean)) < 2e-3
+    assert np.max(np.abs(lse.cpu().numpy() - np.log(n))) < 1e-4
+
+
+def test_empty_sequence_is_noop(gpu_lib):
+    h3 = gpu_lib
+    cfg = h3.rope_cfg()
+    x = torch.zeros((1, 2, 128), dtype=torch.bfloat16, device="cuda")
+    o = torch.full_like(x, 3.0)
+    h3.rope_qk(cfg, None, x, x, None, None, 0, 2, 256)
+    h3.forward(cfg, None, 1, x, x, x, o, None, 0, 2, 256, 256)
+    torch.cuda.synchronize()
+    assert torch.all(o == 3.0)
+
+
+def _sampled_rows(segs, n, count, seed):
+    rows = [0, n - 1]
+    r = 0
+    for s in segs:                        # first and last row of every segment
+        m = s.frames * s.grid_h * s.grid_w
+        if m:
+            rows += [r, r + m - 1]
+        r += m
+    rows += np.random.default_rng(seed).integers(0, n, count).tolist()
+    return np.unique(np.array(rows))
+
+
+@pytest.mark.parametrize("name,heads", [("4s", [0, 41]), ("5s", [0, 17, 41]), ("ref2va", [5, 40]),
+                                        ("15s", [3])])
+def test_forward_full_size_sampled(gpu_lib, name, heads):
+    """Full-size workloads in the timed launch configuration, checked on sampled rows and heads."""
+    h3 = gpu_lib
+    h, segs, q, k, v = inputs(name)
+    n = W.n_tokens(segs)
+    print("config %s n=%d h=%d" % (name, n, h), flush=True)
+    o, lse = run_gpu(h3, segs, q, k, v)
+    rows = _sampled_rows(segs, n, 48, 11)
+    og = host_bits(o[torch.from_numpy(rows).cuda()][:, heads])
+    lg = lse[heads][:, torch.from_numpy(rows).cuda()].cpu().numpy()
+    c = oracle.build_coords(segs)
+    o_ref, lse_ref = oracle.attention(f64(q[:, heads]), f64(k[:, heads]), f64(v[:, heads]), c, SEC, TH,
+                                      rows=rows)
+    check(og, lg, o_ref, lse_ref, name)
+    # properties that hold at any size: every output row finite, |O| <= max |V|
+    of = o.float()
+    assert torch.isfinite(of).all()
+    vmax = float(f64(np.array([np.max(v & np.uint16(0x7FFF))], np.uint16))[0])   # largest |V|
+    assert float(of.abs().max()) <= vmax * (1 + 2 ** -8)

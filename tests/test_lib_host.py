@@ -1,0 +1,163 @@
+"""Host-side checks of libh3attn: it loads, exports every declared symbol, its
+coordinate builder is bit-exact against the oracle, and its argument checks
+reject bad calls before touching a device (no GPU needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def h3():
+    import stream_audio_video_amd as h3
+    h3.load_library()
+    return h3
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "h3attn.h")).read()
+    return sorted(set(re.findall(r"\b(h3attn_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol(h3):
+    decl = _declared()
+    assert set(decl) == set(h3.EXPORTED)
+    lib = h3.load_library()
+    for name in decl:
+        assert hasattr(lib, name)
+    out = subprocess.run(["nm", "-D", "--defined-only", h3._LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (h3attn_\w+)", out))
+    assert set(decl) <= exported
+    assert "gfx950" in h3.version()
+
+
+@pytest.mark.parametrize("name", list(W.CONFIGS))
+def test_coords_bit_exact_vs_oracle(h3, name):
+    _, segs = W.CONFIGS[name]
+    a = h3.build_coords(segs)
+    b = oracle.build_coords(segs)
+    assert a.shape == b.shape == (W.CONFIG_TOKENS[name], 3)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_coords_fuzz_bit_exact(h3):
+    rng = np.random.default_rng(1234)
+    for trial in range(1000):
+        segs = []
+        for _ in range(rng.integers(0, 6)):
+            kind = int(rng.integers(0, 3))
+            frames = int(rng.integers(0, 7))
+            if kind == W.TEXT:
+                gh, gw = 1, 1
+            elif kind == W.AUDIO:
+                gh, gw = 1, int(rng.integers(1, 4))
+            else:
+                gh, gw = int(rng.integers(1, 50)), int(rng.integers(1, 90))
+            t0 = int(rng.integers(-(2 ** 22), 2 ** 22))
+            dt = int(rng.integers(-40, 41))
+            segs.append(W.Segment(kind, frames, gh, gw, t0, dt))
+        a = h3.build_coords(segs)
+        b = oracle.build_coords(segs)
+        assert a.shape == b.shape
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), (trial, segs)
+
+
+def test_coords_count_only_and_capacity(h3):
+    lib = h3.load_library()
+    _, segs = W.CONFIGS["tiny"]
+    arr = h3._segments(segs)
+    n = ctypes.c_int64(-1)
+    assert lib.h3attn_build_coords(arr, len(segs), None, 0, ctypes.byref(n)) == 0 and n.value == 64
+    buf = np.full((63, 3), 7.0, np.float32)
+    rc = lib.h3attn_build_coords(arr, len(segs), buf.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), 63,
+                                 ctypes.byref(n))
+    assert rc == h3.H3ATTN_ERANGE and n.value == 64
+    assert np.all(buf == 7.0)          # nothing written on error
+    assert lib.h3attn_build_coords(arr, len(segs), None, 0, None) == h3.H3ATTN_EINVAL
+    assert lib.h3attn_build_coords(None, 1, None, 0, ctypes.byref(n)) == h3.H3ATTN_EINVAL
+    assert h3.build_coords([]).shape == (0, 3)
+
+
+@pytest.mark.parametrize("seg,code", [
+    (W.Segment(3, 1, 1, 1, 0, 3), -1),            # unknown kind
+    (W.Segment(W.TEXT, 4, 2, 1, 0, 3), -1),       # text with a grid
+    (W.Segment(W.AUDIO, 4, 2, 2, 0, 3), -1),      # audio with grid_h
+    (W.Segment(W.VIDEO, -1, 2, 2, 0, 20), -1),    # negative frames
+    (W.Segment(W.VIDEO, 1, 0, 2, 0, 20), -1),     # empty grid
+    (W.Segment(W.TEXT, 2, 1, 1, 2 ** 24, 3), -2),            # t not exact in binary32
+    (W.Segment(W.TEXT, 3, 1, 1, 2 ** 24 - 4, 3), -2),        # last t out of range
+])
+def test_coords_rejects(h3, seg, code):
+    with pytest.raises(h3.H3AttnError) as e:
+        h3.build_coords([seg])
+    assert e.value.code == code
+
+
+def _cfg(h3, **kw):
+    c = h3.rope_cfg()
+    for k, v in kw.items():
+        if k == "sec":
+            c.sec = (ctypes.c_int32 * 3)(*v)
+        elif k == "theta":
+            c.theta = (ctypes.c_double * 3)(*v)
+        else:
+            setattr(c, k, v)
+    return c
+
+
+BAD_CFGS = [dict(head_dim=64), dict(sec=(32, 48, 40)), dict(sec=(31, 49, 48)), dict(sec=(-2, 82, 48)),
+            dict(theta=(1e4, 0.0, 1e4)), dict(theta=(1e4, float("nan"), 1e4))]
+
+
+@pytest.mark.parametrize("kw", BAD_CFGS)
+def test_abi_rejects_bad_cfg(h3, kw):
+    lib = h3.load_library()
+    cfg = _cfg(h3, **kw)
+    p = 1 << 20
+    assert lib.h3attn_rope_qk(ctypes.byref(cfg), p, p, p, None, None, 64, 2, 256, None) == h3.H3ATTN_EINVAL
+    assert lib.h3attn_forward(ctypes.byref(cfg), p, 1, p, p, p, p * 4, None, 64, 2, 256, 256, 0.0,
+                              None) == h3.H3ATTN_EINVAL
+
+
+def test_abi_rejects_bad_geometry(h3):
+    lib = h3.load_library()
+    cfg = h3.rope_cfg()
+    P = 1 << 20
+    rq = lambda *a: lib.h3attn_rope_qk(ctypes.byref(cfg), *a)
+    fw = lambda *a: lib.h3attn_forward(ctypes.byref(cfg), *a)
+    E, R = h3.H3ATTN_EINVAL, h3.H3ATTN_ERANGE
+    assert rq(P, None, None, None, None, 64, 2, 256, None) == E              # nothing to rotate
+    assert rq(P, P, None, None, None, 64, 2, 256, None) == E                 # q_in without q_out
+    assert rq(P, P + 2, P + 2, None, None, 64, 2, 256, None) == E            # misaligned
+    assert rq(P, P, P, None, None, 64, 2, 200, None) == E                    # stride < H*D
+    assert rq(P, P, P, None, None, 64, 2, 260, None) == E                    # stride not a multiple of 8
+    assert rq(P, P, P, None, None, -1, 2, 256, None) == E                    # negative rows
+    assert rq(P, P, P, None, None, 64, 0, 256, None) == E                    # no heads
+    assert rq(None, P, P, None, None, 64, 2, 256, None) == E                 # coords missing
+    assert rq(P, P, P, None, None, 2 ** 22, 42, 5376, None) == R             # offsets overflow 32 bits
+    assert rq(P, P, P, None, None, 0, 2, 256, None) == 0                     # empty: no-op
+    Q, K, V, O = P, 2 * P, 3 * P, 4 * P
+    assert fw(P, 1, None, K, V, O, None, 64, 2, 256, 256, 0.0, None) == E    # null q
+    assert fw(P, 1, Q, K, V, None, None, 64, 2, 256, 256, 0.0, None) == E    # null o
+    assert fw(P, 1, Q, K, V, O + 8, None, 64, 2, 256, 256, 0.0, None) == E   # misaligned o
+    assert fw(P, 1, Q, K, V, O, P + 2, 64, 2, 256, 256, 0.0, None) == E      # misaligned lse
+    assert fw(P, 1, Q, K, V, Q, None, 64, 2, 256, 256, 0.0, None) == E       # o aliases q
+    assert fw(P, 1, Q, K, V, V + 1024, None, 64, 2, 256, 256, 0.0, None) == E  # o overlaps v
+    assert fw(None, 1, Q, K, V, O, None, 64, 2, 256, 256, 0.0, None) == E    # rope_q without coords
+    assert fw(P, 1, Q, K, V, O, None, 64, 2, 256, 128, 0.0, None) == E       # o stride too small
+    assert fw(P, 1, Q, K, V, O, None, 64, 2, 256, 256, float("inf"), None) == E
+    assert fw(P, 1, Q, K, V, O, None, 2 ** 22, 42, 5376, 5376, 0.0, None) == R
+    assert fw(P, 1, Q, K, V, O, None, 0, 2, 256, 256, 0.0, None) == 0        # empty: no-op
+
+
+def test_strerror(h3):
+    for code in (0, -1, -2, -3, -4, 99):
+        assert isinstance(h3.strerror(code), str) and h3.strerror(code)
