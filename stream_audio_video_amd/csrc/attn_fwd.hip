@@ -5,57 +5,81 @@
 // Video, and Stereo Audio", section 6).  K arrives already rotated; Q is rotated
 // in registers while its tile is loaded (or arrives rotated, rope_q == 0).
 //
-// Work split.  A workgroup of kWaves waves owns kBM = 32 * kWaves query rows of
-// one head; each wave owns 32 query rows and keeps their rotated Q in
-// registers for the whole kernel.  The workgroup streams the head's K and V in
-// tiles of kBN keys through LDS (double-buffered, one barrier per tile; the
-// next tile's global loads are in flight while the current one is computed).
+// Work split.  A workgroup of kWaves waves owns 32 * kWaves query rows of one
+// head; each wave owns 32 query rows and keeps their rotated Q in registers for
+// the whole kernel.  The workgroup streams the head's K and V in tiles of kBN
+// keys through LDS: double-buffered, one barrier per tile, the next tile's
+// buffer loads in flight while the current tile is computed.  The loads use a
+// buffer descriptor rebased on every tile, so rows past the end of the sequence
+// read as zero without any per-lane test.
 //
 // Both products run on v_mfma_f32_32x32x16_bf16 in transposed form so that a
 // query is a column of every accumulator:
 //   S^T[key][query] = K~ . Q~^T   (A = K tile rows from LDS, B = Q~ registers)
-//   O^T[d][query]  += V^T . P^T    (A = V^T from LDS, B = P straight from the
-//                                   S^T accumulators, converted to bf16)
-// With queries in columns, every lane holds one query and 16 of its scores, so
-// the row max is an in-lane max plus one exchange with the lane 32 away, and
-// the row sum needs no exchange until the end.  The contraction order of the PV
-// product is free, so the keys are numbered to match the accumulator layout;
-// V is written transposed into LDS in that key order.
+//   O^T[d][query]  += V^T . P^T    (A = V^T read from the row-major V tile with
+//                                   ds_read_b64_tr_b16, B = P taken straight
+//                                   from the S^T accumulators as bf16)
+// With queries in columns, every lane holds one query and 16 of its scores per
+// 32-key block, so the row max is an in-lane max plus one exchange with the
+// lane 32 away, and the row sum stays per lane until the end.  The contraction
+// order of the PV product is free, so the keys fed to each PV step are the ones
+// the S^T accumulator layout leaves in that lane.
 //
 // Online softmax in base 2 with a lazy rescale: the running reference max of a
 // row is raised (and O, l rescaled) only when a tile's max exceeds it by more
 // than 2^8 in probability, so the rescale is skipped on almost every tile and
 // exp2 arguments stay <= 8.  The result is exact up to rounding either way.
+// The row sum is accumulated from the bf16-rounded P (v_dot2 against ones),
+// i.e. from exactly the weights that multiply V.
 #include "launch.hpp"
 
 namespace h3 {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8;
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kBM = 32 * kWaves;     // query rows per workgroup
-constexpr int kBN = 64;              // keys per tile
-constexpr int kKStr = kHeadDim + 8;  // LDS row stride of the K tile, elements (272 B)
-constexpr int kVStr = kBN + 8;       // LDS row stride of the V^T tile, elements (144 B)
-constexpr float kLazyLog2 = 8.0f;    // rescale only when the max grows by more than 2^8
+constexpr int kBM = 32 * kWaves;             // query rows per workgroup
+constexpr int kBN = 64;                      // keys per tile
+constexpr int kKStr = kHeadDim + 8;          // LDS row stride of the K tile, elements (272 B)
+constexpr int kVStr = kHeadDim + 16;         // LDS row stride of the V tile, elements (288 B)
+constexpr int kKTile = kBN * kKStr;          // elements per K buffer
+constexpr int kVTile = kBN * kVStr;          // elements per V buffer
+constexpr int kChunks = kBN * 16 / kThreads; // 16-byte chunks per thread per tensor per tile
+constexpr int kRowsPerPass = kThreads / 16;  // rows covered by one pass of all threads
+constexpr float kLazyLog2 = 8.0f;            // rescale only when the max grows by more than 2^8
+constexpr int kRsrcFlags = 0x00020000;       // raw buffer, 32-bit data format
 
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8_t, x); }
+struct NoMask { static constexpr bool value = false; };
+struct Mask { static constexpr bool value = true; };
 
 __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Position inside a 16-key group of the V^T tile for the 4-key run starting at
-// key 4r (r = 0..3): runs are stored in the order 0, 2, 1, 3 so that the 8 keys
-// one lane feeds to a PV step (keys 4h..4h+3 and 8+4h..8+4h+3) are contiguous.
-__device__ __forceinline__ int vt_run_slot(int r) { return ((r & 1) << 1) | (r >> 1); }
+// max over the two lanes that hold the same query (l and l ^ 32)
+__device__ __forceinline__ float pair_max(float x) {
+  const u32x2_t r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const u32x2_t r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t ks[2][kBN * kKStr];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[2][kHeadDim * kVStr];
+  __shared__ __attribute__((aligned(16))) uint16_t ks[2 * kKTile];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[2 * kVTile];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -68,7 +92,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   const int qrow = qb * kBM + wave * 32 + col;
   const bool qvalid = qrow < a.n;
 
-  // ---- Q~ fragment: B operand of S^T, lane holds dims 16c + 8hf .. +7 of its query
+  // ---- Q~ fragment: B operand of S^T; lane holds dims 16c + 8hf .. +7 of its query
   bf16x8_t qf[8];
   {
     const uint16_t* qp = a.q + (qvalid ? qrow : 0) * a.stride_qkv + head * kHeadDim + 8 * hf;
@@ -93,54 +117,57 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
         }
         x = make_uint4(w[0], w[1], w[2], w[3]);
       }
-      qf[c] = as_bf16x8(x);
+      qf[c] = __builtin_bit_cast(bf16x8_t, x);
     }
   }
 
-  // ---- K / V tile loaders
-  const uint16_t* kbase_p = a.k + head * kHeadDim;
-  const uint16_t* vbase_p = a.v + head * kHeadDim;
-  const int kd = (tid & 15) * 8;      // K: 16-byte chunk of a key row
-  const int krow = tid >> 4;          // K: key rows krow + 16 r
-  const int vd = (tid & 15) * 8;      // V: dims vd .. vd+7
-  const int vg = tid >> 4;            // V: keys 4vg .. 4vg+3
-  uint4 kr[4], vr[4];
-
-  auto load_tile = [&](int key0) {
+  // ---- K / V tile loads: thread covers rows (tid >> 4) + kRowsPerPass * r, bytes 16 * (tid & 15)
+  const int row_bytes = a.stride_qkv * 2;
+  const int64_t head_off = int64_t(head) * kHeadDim * 2;
+  const int64_t span = int64_t(a.n - 1) * row_bytes + kHeadDim * 2;   // bytes from the head base to its last byte
+  const char* kbase = reinterpret_cast<const char*>(a.k) + head_off;
+  const char* vbase = reinterpret_cast<const char*>(a.v) + head_off;
+  int voff[kChunks];
+  int lds_k_st[kChunks], lds_v_st[kChunks];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = key0 + krow + 16 * r;
-      kr[r] = key < a.n ? *reinterpret_cast<const uint4*>(kbase_p + key * a.stride_qkv + kd)
-                        : make_uint4(0, 0, 0, 0);
-    }
+  for (int r = 0; r < kChunks; ++r) {
+    const int row = (tid >> 4) + kRowsPerPass * r;
+    voff[r] = row * row_bytes + (tid & 15) * 16;
+    lds_k_st[r] = row * kKStr + (tid & 15) * 8;
+    lds_v_st[r] = row * kVStr + (tid & 15) * 8;
+  }
+  u32x4_t kr[kChunks], vr[kChunks];
+  auto load_tile = [&](int t) {
+    const int64_t off = int64_t(t) * kBN * row_bytes;
+    const int rec = static_cast<int>(static_cast<uint32_t>(span - off));   // < 2^32 by the size check
+    const __amdgpu_buffer_rsrc_t kd = __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + off), 0, rec, kRsrcFlags);
+    const __amdgpu_buffer_rsrc_t vd = __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + off), 0, rec, kRsrcFlags);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = key0 + 4 * vg + i;
-      vr[i] = key < a.n ? *reinterpret_cast<const uint4*>(vbase_p + key * a.stride_qkv + vd)
-                        : make_uint4(0, 0, 0, 0);
-    }
+    for (int r = 0; r < kChunks; ++r)
+      kr[r] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(kd, voff[r], 0, 0));
+#pragma unroll
+    for (int r = 0; r < kChunks; ++r)
+      vr[r] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vd, voff[r], 0, 0));
   };
-
-  const int vslot = 16 * (vg >> 2) + 4 * vt_run_slot(vg & 3);
+  lds_u16* ksl = (lds_u16*)ks;
+  lds_u16* vsl = (lds_u16*)vs;
   auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      *reinterpret_cast<uint4*>(&ks[buf][(krow + 16 * r) * kKStr + kd]) = kr[r];
-    const uint32_t v0[4] = {vr[0].x, vr[0].y, vr[0].z, vr[0].w};
-    const uint32_t v1[4] = {vr[1].x, vr[1].y, vr[1].z, vr[1].w};
-    const uint32_t v2[4] = {vr[2].x, vr[2].y, vr[2].z, vr[2].w};
-    const uint32_t v3[4] = {vr[3].x, vr[3].y, vr[3].z, vr[3].w};
+    for (int r = 0; r < kChunks; ++r)
+      *reinterpret_cast<lds_u32x4*>(ksl + buf * kKTile + lds_k_st[r]) = kr[r];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      // dim vd + 2w: low halves of the four keys; dim vd + 2w + 1: high halves
-      const uint2 lo = make_uint2(__builtin_amdgcn_perm(v1[w], v0[w], 0x05040100u),
-                                  __builtin_amdgcn_perm(v3[w], v2[w], 0x05040100u));
-      const uint2 hi = make_uint2(__builtin_amdgcn_perm(v1[w], v0[w], 0x07060302u),
-                                  __builtin_amdgcn_perm(v3[w], v2[w], 0x07060302u));
-      *reinterpret_cast<uint2*>(&vt[buf][(vd + 2 * w) * kVStr + vslot]) = lo;
-      *reinterpret_cast<uint2*>(&vt[buf][(vd + 2 * w + 1) * kVStr + vslot]) = hi;
-    }
+    for (int r = 0; r < kChunks; ++r)
+      *reinterpret_cast<lds_u32x4*>(vsl + buf * kVTile + lds_v_st[r]) = vr[r];
   };
+
+  // per-lane LDS read bases
+  // K (A of S^T): row = key 32b + col, elements 16c + 8hf
+  const int k_rd = col * kKStr + 8 * hf;
+  // V^T (A of O^T) via transpose reads: in each 16-lane group g, lanes 4r + j
+  // address row (16kc + 8c + 4(g >> 1) + r), columns 32db + 16(g & 1) + 4j; lane i
+  // of the group receives column i of the four rows.
+  const int g = lane >> 4;
+  const int v_rd = (4 * (g >> 1) + ((lane >> 2) & 3)) * kVStr + 16 * (g & 1) + 4 * (lane & 3);
 
   f32x16_t oacc[4];
 #pragma unroll
@@ -148,83 +175,97 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   float m_ref = -__builtin_inff();
   float l_part = 0.0f;
   const float c2 = a.scale_log2;
+  const bf16x2_t ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
-  const int ntiles = (a.n + kBN - 1) / kBN;
-  load_tile(0);
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    store_tile(buf);
-    __syncthreads();
-    if (t + 1 < ntiles) load_tile((t + 1) * kBN);
+  auto compute = [&](int buf, int key0, auto masked) {
+    constexpr bool kMask = decltype(masked)::value;
+    const lds_u16* kt = ksl + buf * kKTile + k_rd;
+    const lds_u16* vt = vsl + buf * kVTile + v_rd;
 
-    // S^T = K~ Q~^T for two 32-key blocks
-    f32x16_t s[2];
+    // S^T = K~ Q~^T for the two 32-key blocks of the tile
+    f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      s[b] = f32x16_t{};
-      const uint16_t* kp = &ks[buf][(32 * b + col) * kKStr + 8 * hf];
-#pragma unroll
-      for (int c = 0; c < 8; ++c)
-        s[b] = mfma32(*reinterpret_cast<const bf16x8_t*>(kp + 16 * c), qf[c], s[b]);
+    for (int c = 0; c < 8; ++c) {
+      const bf16x8_t k0 = *reinterpret_cast<const lds_bf16x8*>(kt + 16 * c);
+      const bf16x8_t k1 = *reinterpret_cast<const lds_bf16x8*>(kt + 32 * kKStr + 16 * c);
+      s0 = mfma32(k0, qf[c], s0);
+      s1 = mfma32(k1, qf[c], s1);
     }
 
-    // keys past the end of the sequence (last tile only) take no weight
-    const int key0 = t * kBN;
-    if (key0 + kBN > a.n) {
+    if constexpr (kMask) {
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = key0 + 32 * b + 8 * (r >> 2) + 4 * hf + (r & 3);
-          if (key >= a.n) s[b][r] = -__builtin_inff();
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + 8 * (r >> 2) + 4 * hf + (r & 3);
+        if (key >= a.n) s0[r] = -__builtin_inff();
+        if (key + 32 >= a.n) s1[r] = -__builtin_inff();
+      }
     }
 
-    float mt = s[0][0];
+    // NaN-propagating maximum: lowers to v_maximum3_f32 with no input canonicalisation
+    float mt = __builtin_elementwise_maximum(s0[0], s1[0]);
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[b][r]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    for (int r = 1; r < 16; ++r) mt = __builtin_elementwise_maximum(mt, __builtin_elementwise_maximum(s0[r], s1[r]));
+    mt = pair_max(mt);
 
     const bool need = (mt - m_ref) * c2 > kLazyLog2;
     if (__builtin_amdgcn_ballot_w64(need) != 0) {
-      const float m_new = fmaxf(m_ref, mt);
+      const float m_new = __builtin_elementwise_maximum(m_ref, mt);
       const float alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * c2);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+      for (int i = 0; i < 4; ++i) oacc[i] *= alpha;
       l_part *= alpha;
       m_ref = m_new;
     }
     const float nm = -m_ref * c2;
 
-    // P = exp2(S * c - m * c) -> bf16, the B operand of the PV product
+    // P = exp2(S c - m c) as bf16: pb[b][half] is the B operand of PV chunk 2b + half
     bf16x8_t pb[2][2];
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], c2, nm));
-        l_part += p;
-        pb[b][r >> 3][r & 7] = static_cast<__bf16>(p);
-      }
+    for (int r = 0; r < 16; r += 2) {
+      bf16x2_t p0, p1;
+      p0[0] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], c2, nm)));
+      p0[1] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s0[r + 1], c2, nm)));
+      p1[0] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], c2, nm)));
+      p1[1] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s1[r + 1], c2, nm)));
+      l_part = __builtin_amdgcn_fdot2_f32_bf16(p0, ones, l_part, false);
+      l_part = __builtin_amdgcn_fdot2_f32_bf16(p1, ones, l_part, false);
+      pb[0][r >> 3][r & 7] = p0[0];
+      pb[0][r >> 3][(r & 7) + 1] = p0[1];
+      pb[1][r >> 3][r & 7] = p1[0];
+      pb[1][r >> 3][(r & 7) + 1] = p1[1];
+    }
 
-    // O^T += V^T P^T over four 16-key chunks, four 32-dim blocks
+    // O^T += V^T P^T over four 16-key chunks and four 32-dim blocks
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const bf16x8_t va =
-            *reinterpret_cast<const bf16x8_t*>(&vt[buf][(32 * db + col) * kVStr + 16 * kc + 8 * hf]);
-        oacc[db] = mfma32(va, pb[kc >> 1][kc & 1], oacc[db]);
+        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            reinterpret_cast<lds_i16x4*>(const_cast<lds_u16*>(vt + (16 * kc) * kVStr + 32 * db)));
+        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            reinterpret_cast<lds_i16x4*>(const_cast<lds_u16*>(vt + (16 * kc + 8) * kVStr + 32 * db)));
+        const i16x4_t both[2] = {lo, hi};
+        oacc[db] = mfma32(__builtin_bit_cast(bf16x8_t, both), pb[kc >> 1][kc & 1], oacc[db]);
       }
     }
+  };
+
+  // all tiles but the last are full; the last one masks keys >= n (a no-op when
+  // n is a multiple of kBN), so the steady-state loop has a single body
+  const int ntiles = (a.n + kBN - 1) / kBN;
+  load_tile(0);
+  store_tile(0);
+  for (int t = 0; t + 1 < ntiles; ++t) {
+    __syncthreads();
+    load_tile(t + 1);
+    compute(t & 1, t * kBN, NoMask{});
+    store_tile((t + 1) & 1);
   }
+  __syncthreads();
+  compute((ntiles - 1) & 1, (ntiles - 1) * kBN, Mask{});
 
   // ---- epilogue: O = O^T / l, LSE = m * scale + ln l
-  const float l_tot = l_part + __shfl_xor(l_part, 32);
+  const float l_tot = pair_sum(l_part);
   if (qvalid) {
     const float inv = 1.0f / l_tot;
     uint16_t* op = a.o + qrow * a.stride_o + head * kHeadDim;
