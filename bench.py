@@ -63,7 +63,19 @@ def main():
     ap.add_argument("--config", default="5s", choices=list(W.CONFIGS))
     ap.add_argument("--mode", default="fused", choices=["fused", "prerotated"])
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing (0 = skip)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a device-to-device copy of MIB MiB three times (scales HBM byte counters)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        nbytes = args.calibrate_copy << 20
+        src = torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_dispatch": nbytes, "dispatches": 3}))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the path is single-GPU (use --gpus 1)", file=sys.stderr)
         sys.exit(2)

@@ -40,26 +40,34 @@ def _run(cmd):
     return out
 
 
-def build(verbose=False, save_temps=False):
-    """Compile every source and link libh3attn.so.  Always rebuilds."""
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose=False, save_temps=False, out=None, extra_flags=(), build_dir=None, csrc=None):
+    """Compile every source and link the library (default: libh3attn.so in the package).
+
+    extra_flags are appended to the HIP compile lines (e.g. -D overrides of the
+    kernels' tile constants); out, build_dir and csrc redirect the products and
+    the source directory.  Always rebuilds.
+    """
+    out = out or LIB
+    bdir = build_dir or BUILD
+    src_dir = csrc or CSRC
+    os.makedirs(bdir, exist_ok=True)
     jobs = []
     for src in HIP_SOURCES:
-        obj = os.path.join(BUILD, src + ".o")
+        obj = os.path.join(bdir, src + ".o")
         extra = ["-save-temps=obj"] if save_temps else []
-        jobs.append([HIPCC] + HIP_FLAGS + extra + ["-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append([HIPCC] + HIP_FLAGS + list(extra_flags) + extra + ["-c", os.path.join(src_dir, src), "-o", obj])
     for src in HOST_SOURCES:
-        obj = os.path.join(BUILD, src + ".o")
-        jobs.append(["g++"] + HOST_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj])
+        obj = os.path.join(bdir, src + ".o")
+        jobs.append(["g++"] + HOST_FLAGS + ["-c", os.path.join(src_dir, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
-        for out in ex.map(_run, jobs):
-            if verbose and out.strip():
-                print(out)
-    objs = [os.path.join(BUILD, s + ".o") for s in HIP_SOURCES + HOST_SOURCES]
-    tmp = LIB + ".tmp"
+        for log in ex.map(_run, jobs):
+            if verbose and log.strip():
+                print(log)
+    objs = [os.path.join(bdir, s + ".o") for s in HIP_SOURCES + HOST_SOURCES]
+    tmp = out + ".tmp"
     _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

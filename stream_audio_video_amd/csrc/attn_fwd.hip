@@ -8,8 +8,8 @@
 // Work split.  A workgroup of kWaves waves owns 32 * kWaves query rows of one
 // head; each wave owns 32 query rows and keeps their rotated Q in registers for
 // the whole kernel.  The workgroup streams the head's K and V in tiles of kBN
-// keys through LDS: double-buffered, one barrier per tile, the next tile's
-// buffer loads in flight while the current tile is computed.  The loads use a
+// keys through LDS, double-buffered with one barrier per tile: the next tile's
+// loads are in flight while the current tile is computed.  The loads use a
 // buffer descriptor rebased on every tile, so rows past the end of the sequence
 // read as zero without any per-lane test.
 //
@@ -25,12 +25,16 @@
 // order of the PV product is free, so the keys fed to each PV step are the ones
 // the S^T accumulator layout leaves in that lane.
 //
-// Online softmax in base 2 with a lazy rescale: the running reference max of a
-// row is raised (and O, l rescaled) only when a tile's max exceeds it by more
-// than 2^8 in probability, so the rescale is skipped on almost every tile and
-// exp2 arguments stay <= 8.  The result is exact up to rounding either way.
-// The row sum is accumulated from the bf16-rounded P (v_dot2 against ones),
-// i.e. from exactly the weights that multiply V.
+// Online softmax in base 2, biased.  Q~ is pre-scaled by scale * log2(e)
+// (after its own bf16 rounding, so both rope routes stay bit-identical), and
+// every score chain starts from an accumulator holding -m, the row's running
+// reference max in those units: the MFMA itself returns s - m, so P = exp2 of
+// the accumulator with no per-score arithmetic.  The reference is raised only
+// when a tile's probabilities get large: each lane sums its tile's P (v_dot2 on
+// the bf16 P, i.e. exactly the weights that multiply V); if any lane's sum
+// exceeds 2^8 - which bounds every single P - the wave takes a rare slow path
+// that raises the reference to the new max, rescales O and l, and recomputes
+// the tile.  So every P is <= 2^8 and the result is exact up to rounding.
 #include "launch.hpp"
 
 namespace h3 {
@@ -47,24 +51,38 @@ typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8;
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
 
-constexpr int kWaves = 4;
+#ifndef H3_ATTN_WAVES
+#define H3_ATTN_WAVES 4
+#endif
+constexpr int kWaves = H3_ATTN_WAVES;
+
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;             // query rows per workgroup
 constexpr int kBN = 64;                      // keys per tile
 constexpr int kKStr = kHeadDim + 8;          // LDS row stride of the K tile, elements (272 B)
-constexpr int kVStr = kHeadDim + 16;         // LDS row stride of the V tile, elements (288 B)
+#ifndef H3_ATTN_VSTR
+#define H3_ATTN_VSTR (kHeadDim + 32)
+#endif
+// LDS row stride of the V tile, elements: 320 B puts the four rows and two
+// column halves of each transpose read on disjoint banks
+constexpr int kVStr = H3_ATTN_VSTR;
 constexpr int kKTile = kBN * kKStr;          // elements per K buffer
 constexpr int kVTile = kBN * kVStr;          // elements per V buffer
 constexpr int kChunks = kBN * 16 / kThreads; // 16-byte chunks per thread per tensor per tile
 constexpr int kRowsPerPass = kThreads / 16;  // rows covered by one pass of all threads
-constexpr float kLazyLog2 = 8.0f;            // rescale only when the max grows by more than 2^8
+constexpr float kMaxTileSum = 256.0f;        // a lane's tile sum of P above 2^8 raises the reference
 constexpr int kRsrcFlags = 0x00020000;       // raw buffer, 32-bit data format
 
-struct NoMask { static constexpr bool value = false; };
-struct Mask { static constexpr bool value = true; };
+struct True { static constexpr bool value = true; };
+struct False { static constexpr bool value = false; };
 
 __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// two bf16 (low, high) times f, rounded back to bf16
+__device__ __forceinline__ uint32_t scale_word(uint32_t w, float f) {
+  return pack_bf16x2(__uint_as_float(w << 16) * f, __uint_as_float(w & 0xffff0000u) * f);
 }
 
 // max over the two lanes that hold the same query (l and l ^ 32)
@@ -117,6 +135,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
         }
         x = make_uint4(w[0], w[1], w[2], w[3]);
       }
+      // pre-scale by scale * log2(e), rounding once more to bf16
+      x = make_uint4(scale_word(x.x, a.scale_log2), scale_word(x.y, a.scale_log2),
+                     scale_word(x.z, a.scale_log2), scale_word(x.w, a.scale_log2));
       qf[c] = __builtin_bit_cast(bf16x8_t, x);
     }
   }
@@ -137,24 +158,33 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
     lds_v_st[r] = row * kVStr + (tid & 15) * 8;
   }
   u32x4_t kr[kChunks], vr[kChunks];
-  auto load_tile = [&](int t) {
+  auto rsrc = [&](const char* base, int t) {
     const int64_t off = int64_t(t) * kBN * row_bytes;
-    const int rec = static_cast<int>(static_cast<uint32_t>(span - off));   // < 2^32 by the size check
-    const __amdgpu_buffer_rsrc_t kd = __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + off), 0, rec, kRsrcFlags);
-    const __amdgpu_buffer_rsrc_t vd = __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + off), 0, rec, kRsrcFlags);
+    // bytes left from this tile's first row; 0 past the end, so loads there read zeros
+    const int64_t left = span - off > 0 ? span - off : 0;
+    const int rec = static_cast<int>(static_cast<uint32_t>(left));   // < 2^32 by the size check
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + off), 0, rec, kRsrcFlags);
+  };
+  auto load_k = [&](int t) {
+    const __amdgpu_buffer_rsrc_t d = rsrc(kbase, t);
 #pragma unroll
     for (int r = 0; r < kChunks; ++r)
-      kr[r] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(kd, voff[r], 0, 0));
+      kr[r] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(d, voff[r], 0, 0));
+  };
+  auto load_v = [&](int t) {
+    const __amdgpu_buffer_rsrc_t d = rsrc(vbase, t);
 #pragma unroll
     for (int r = 0; r < kChunks; ++r)
-      vr[r] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vd, voff[r], 0, 0));
+      vr[r] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(d, voff[r], 0, 0));
   };
   lds_u16* ksl = (lds_u16*)ks;
   lds_u16* vsl = (lds_u16*)vs;
-  auto store_tile = [&](int buf) {
+  auto store_k = [&](int buf) {
 #pragma unroll
     for (int r = 0; r < kChunks; ++r)
       *reinterpret_cast<lds_u32x4*>(ksl + buf * kKTile + lds_k_st[r]) = kr[r];
+  };
+  auto store_v = [&](int buf) {
 #pragma unroll
     for (int r = 0; r < kChunks; ++r)
       *reinterpret_cast<lds_u32x4*>(vsl + buf * kVTile + lds_v_st[r]) = vr[r];
@@ -172,70 +202,70 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   f32x16_t oacc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) oacc[i] = f32x16_t{};
-  float m_ref = -__builtin_inff();
+  float m_ref = 0.0f;          // running reference max of the row, log2 units
+  f32x16_t cinit = f32x16_t{}; // -m_ref in every entry: the start of each score chain
   float l_part = 0.0f;
-  const float c2 = a.scale_log2;
   const bf16x2_t ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
-  auto compute = [&](int buf, int key0, auto masked) {
-    constexpr bool kMask = decltype(masked)::value;
+  // S^T = K~ Q~^T * scale * log2(e) - m for the two 32-key blocks of K buffer `buf`
+  auto scores = [&](int buf, f32x16_t& s0, f32x16_t& s1) {
     const lds_u16* kt = ksl + buf * kKTile + k_rd;
-    const lds_u16* vt = vsl + buf * kVTile + v_rd;
-
-    // S^T = K~ Q~^T for the two 32-key blocks of the tile
-    f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
+    s0 = mfma32(*reinterpret_cast<const lds_bf16x8*>(kt), qf[0], cinit);
+    s1 = mfma32(*reinterpret_cast<const lds_bf16x8*>(kt + 32 * kKStr), qf[0], cinit);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
+    for (int c = 1; c < 8; ++c) {
       const bf16x8_t k0 = *reinterpret_cast<const lds_bf16x8*>(kt + 16 * c);
       const bf16x8_t k1 = *reinterpret_cast<const lds_bf16x8*>(kt + 32 * kKStr + 16 * c);
       s0 = mfma32(k0, qf[c], s0);
       s1 = mfma32(k1, qf[c], s1);
     }
+  };
 
-    if constexpr (kMask) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = key0 + 8 * (r >> 2) + 4 * hf + (r & 3);
-        if (key >= a.n) s0[r] = -__builtin_inff();
-        if (key + 32 >= a.n) s1[r] = -__builtin_inff();
-      }
-    }
-
-    // NaN-propagating maximum: lowers to v_maximum3_f32 with no input canonicalisation
-    float mt = __builtin_elementwise_maximum(s0[0], s1[0]);
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mt = __builtin_elementwise_maximum(mt, __builtin_elementwise_maximum(s0[r], s1[r]));
-    mt = pair_max(mt);
-
-    const bool need = (mt - m_ref) * c2 > kLazyLog2;
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
-      const float m_new = __builtin_elementwise_maximum(m_ref, mt);
-      const float alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * c2);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) oacc[i] *= alpha;
-      l_part *= alpha;
-      m_ref = m_new;
-    }
-    const float nm = -m_ref * c2;
-
-    // P = exp2(S c - m c) as bf16: pb[b][half] is the B operand of PV chunk 2b + half
-    bf16x8_t pb[2][2];
+  // P = exp2(S) as bf16 (pb[b][half] is the B operand of PV chunk 2b + half);
+  // returns this lane's sum of the tile's P
+  auto probs = [&](const f32x16_t& s0, const f32x16_t& s1, bf16x8_t (&pb)[2][2]) {
+    float lt = 0.0f;
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
       bf16x2_t p0, p1;
-      p0[0] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], c2, nm)));
-      p0[1] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s0[r + 1], c2, nm)));
-      p1[0] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], c2, nm)));
-      p1[1] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s1[r + 1], c2, nm)));
-      l_part = __builtin_amdgcn_fdot2_f32_bf16(p0, ones, l_part, false);
-      l_part = __builtin_amdgcn_fdot2_f32_bf16(p1, ones, l_part, false);
+      p0[0] = static_cast<__bf16>(__builtin_amdgcn_exp2f(s0[r]));
+      p0[1] = static_cast<__bf16>(__builtin_amdgcn_exp2f(s0[r + 1]));
+      p1[0] = static_cast<__bf16>(__builtin_amdgcn_exp2f(s1[r]));
+      p1[1] = static_cast<__bf16>(__builtin_amdgcn_exp2f(s1[r + 1]));
+      lt = __builtin_amdgcn_fdot2_f32_bf16(p0, ones, lt, false);
+      lt = __builtin_amdgcn_fdot2_f32_bf16(p1, ones, lt, false);
       pb[0][r >> 3][r & 7] = p0[0];
       pb[0][r >> 3][(r & 7) + 1] = p0[1];
       pb[1][r >> 3][r & 7] = p1[0];
       pb[1][r >> 3][(r & 7) + 1] = p1[1];
     }
+    return lt;
+  };
 
-    // O^T += V^T P^T over four 16-key chunks and four 32-dim blocks
+  // row max of a tile over both lanes of each query
+  auto tile_max = [&](const f32x16_t& s0, const f32x16_t& s1) {
+    // NaN-propagating maximum: lowers to v_maximum3_f32 with no input canonicalisation
+    float mt = __builtin_elementwise_maximum(s0[0], s1[0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mt = __builtin_elementwise_maximum(mt, __builtin_elementwise_maximum(s0[r], s1[r]));
+    return pair_max(mt);
+  };
+
+  // raise the reference by delta >= 0: shift the live scores, rescale O and l
+  auto raise_ref = [&](float delta, f32x16_t& s0, f32x16_t& s1) {
+    s0 -= delta;
+    s1 -= delta;
+    cinit -= delta;
+    m_ref += delta;
+    const float alpha = __builtin_amdgcn_exp2f(-delta);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) oacc[i] *= alpha;
+    l_part *= alpha;
+  };
+
+  // O^T += V^T P^T over four 16-key chunks and four 32-dim blocks of V buffer `buf`
+  auto pv = [&](int buf, const bf16x8_t (&pb)[2][2]) {
+    const lds_u16* vt = vsl + buf * kVTile + v_rd;
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
 #pragma unroll
@@ -250,19 +280,64 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
     }
   };
 
-  // all tiles but the last are full; the last one masks keys >= n (a no-op when
-  // n is a multiple of kBN), so the steady-state loop has a single body
+  // keys past the end of the sequence take no weight (last tile only)
+  auto mask_tail = [&](f32x16_t& s0, f32x16_t& s1, int key0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = key0 + 8 * (r >> 2) + 4 * hf + (r & 3);
+      if (key >= a.n) s0[r] = -__builtin_inff();
+      if (key + 32 >= a.n) s1[r] = -__builtin_inff();
+    }
+  };
+
+  // One tile: scores, softmax, PV.  The first tile sets the reference max (O and
+  // l are still zero); the last one masks keys >= n.
+  auto step = [&](int t, auto first, auto last) {
+    f32x16_t s0, s1;
+    scores(t & 1, s0, s1);
+    if constexpr (decltype(last)::value) mask_tail(s0, s1, t * kBN);
+    if constexpr (decltype(first)::value) {
+      const float mt = tile_max(s0, s1);
+      s0 -= mt;
+      s1 -= mt;
+      cinit -= mt;
+      m_ref = mt;
+    }
+    bf16x8_t pb[2][2];
+    float lt = probs(s0, s1, pb);
+    if constexpr (!decltype(first)::value) {
+      if (__builtin_amdgcn_ballot_w64(lt > kMaxTileSum) != 0) {
+        raise_ref(__builtin_elementwise_maximum(tile_max(s0, s1), 0.0f), s0, s1);
+        lt = probs(s0, s1, pb);
+      }
+    }
+    l_part += lt;
+    pv(t & 1, pb);
+  };
+  auto load_tile = [&](int t) { load_k(t); load_v(t); };
+  auto store_tile = [&](int buf) { store_k(buf); store_v(buf); };
+
+  // Double-buffered tiles, one barrier per tile: tile t+1 is loaded into
+  // registers while tile t is computed, then stored into the other buffer.
   const int ntiles = (a.n + kBN - 1) / kBN;
   load_tile(0);
   store_tile(0);
-  for (int t = 0; t + 1 < ntiles; ++t) {
-    __syncthreads();
-    load_tile(t + 1);
-    compute(t & 1, t * kBN, NoMask{});
-    store_tile((t + 1) & 1);
-  }
   __syncthreads();
-  compute((ntiles - 1) & 1, (ntiles - 1) * kBN, Mask{});
+  if (ntiles == 1) {
+    step(0, True{}, True{});
+  } else {
+    load_tile(1);
+    step(0, True{}, False{});
+    store_tile(1);
+    for (int t = 1; t + 1 < ntiles; ++t) {
+      __syncthreads();
+      load_tile(t + 1);
+      step(t, False{}, False{});
+      store_tile((t + 1) & 1);
+    }
+    __syncthreads();
+    step(ntiles - 1, False{}, True{});
+  }
 
   // ---- epilogue: O = O^T / l, LSE = m * scale + ln l
   const float l_tot = pair_sum(l_part);
@@ -278,7 +353,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
                                    pack_bf16x2(oacc[db][4 * i + 2] * inv, oacc[db][4 * i + 3] * inv));
         *reinterpret_cast<uint2*>(op + d) = w;
       }
-    if (a.lse != nullptr && hf == 0) a.lse[head * a.n + qrow] = m_ref * a.scale + logf(l_tot);
+    // m_ref is in log2 units of the scaled scores: LSE = (m_ref + log2 l) * ln 2
+    if (a.lse != nullptr && hf == 0) a.lse[head * a.n + qrow] = (m_ref + __log2f(l_tot)) * 0.69314718055994531f;
   }
 }
 
