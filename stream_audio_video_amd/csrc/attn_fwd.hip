@@ -5,13 +5,15 @@
 // Video, and Stereo Audio", section 6).  K arrives already rotated; Q is rotated
 // in registers while its tile is loaded (or arrives rotated, rope_q == 0).
 //
-// Work split.  A workgroup of kWaves waves owns 32 * kWaves query rows of one
-// head; each wave owns 32 query rows and keeps their rotated Q in registers for
-// the whole kernel.  The workgroup streams the head's K and V in tiles of kBN
-// keys through LDS, double-buffered with one barrier per tile: the next tile's
-// loads are in flight while the current tile is computed.  The loads use a
-// buffer descriptor rebased on every tile, so rows past the end of the sequence
-// read as zero without any per-lane test.
+// Work split.  A workgroup of kWaves waves owns kBM = 32 * kQB * kWaves query
+// rows of one head; each wave owns kQB blocks of 32 query rows and keeps their
+// rotated Q in registers for the whole kernel.  Every K or V operand a wave
+// reads from LDS feeds kQB MFMAs (one per query block), which halves the LDS
+// traffic per MFMA at kQB = 2.  The workgroup streams the head's K and V in
+// tiles of kBN keys through LDS, double-buffered with one barrier per tile: the
+// next tile's loads are in flight while the current tile is computed.  The
+// loads use a buffer descriptor rebased on every tile, so rows past the end of
+// the sequence read as zero without any per-lane test.
 //
 // Both products run on v_mfma_f32_32x32x16_bf16 in transposed form so that a
 // query is a column of every accumulator:
@@ -20,10 +22,10 @@
 //                                   ds_read_b64_tr_b16, B = P taken straight
 //                                   from the S^T accumulators as bf16)
 // With queries in columns, every lane holds one query and 16 of its scores per
-// 32-key block, so the row max is an in-lane max plus one exchange with the
-// lane 32 away, and the row sum stays per lane until the end.  The contraction
-// order of the PV product is free, so the keys fed to each PV step are the ones
-// the S^T accumulator layout leaves in that lane.
+// 32-key block, so a row max is an in-lane max plus one exchange with the lane
+// 32 away, and the row sum stays per lane until the end.  The contraction order
+// of the PV product is free, so the keys fed to each PV step are the ones the
+// S^T accumulator layout leaves in that lane.
 //
 // Online softmax in base 2, biased.  Q~ is pre-scaled by scale * log2(e)
 // (after its own bf16 rounding, so both rope routes stay bit-identical), and
@@ -45,24 +47,32 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
 typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8;
-typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
 
 #ifndef H3_ATTN_WAVES
-#define H3_ATTN_WAVES 4
+#define H3_ATTN_WAVES 8
 #endif
-constexpr int kWaves = H3_ATTN_WAVES;
-
-constexpr int kThreads = 64 * kWaves;
-constexpr int kBM = 32 * kWaves;             // query rows per workgroup
-constexpr int kBN = 64;                      // keys per tile
-constexpr int kKStr = kHeadDim + 8;          // LDS row stride of the K tile, elements (272 B)
+#ifndef H3_ATTN_QB
+#define H3_ATTN_QB 1
+#endif
+#ifndef H3_ATTN_BN
+#define H3_ATTN_BN 64
+#endif
 #ifndef H3_ATTN_VSTR
 #define H3_ATTN_VSTR (kHeadDim + 32)
 #endif
+
+constexpr int kWaves = H3_ATTN_WAVES;
+constexpr int kQB = H3_ATTN_QB;              // 32-row query blocks per wave
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBM = 32 * kQB * kWaves;       // query rows per workgroup
+constexpr int kBN = H3_ATTN_BN;              // keys per tile (multiple of 32)
+constexpr int kKB = kBN / 32;                // 32-key blocks per tile
+constexpr int kKStr = kHeadDim + 8;          // LDS row stride of the K tile, elements (272 B)
 // LDS row stride of the V tile, elements: 320 B puts the four rows and two
 // column halves of each transpose read on disjoint banks
 constexpr int kVStr = H3_ATTN_VSTR;
@@ -72,6 +82,7 @@ constexpr int kChunks = kBN * 16 / kThreads; // 16-byte chunks per thread per te
 constexpr int kRowsPerPass = kThreads / 16;  // rows covered by one pass of all threads
 constexpr float kMaxTileSum = 256.0f;        // a lane's tile sum of P above 2^8 raises the reference
 constexpr int kRsrcFlags = 0x00020000;       // raw buffer, 32-bit data format
+static_assert(kBN % 32 == 0 && kChunks >= 1 && kBN * 16 == kChunks * kThreads, "tile shape");
 
 struct True { static constexpr bool value = true; };
 struct False { static constexpr bool value = false; };
@@ -85,7 +96,7 @@ __device__ __forceinline__ uint32_t scale_word(uint32_t w, float f) {
   return pack_bf16x2(__uint_as_float(w << 16) * f, __uint_as_float(w & 0xffff0000u) * f);
 }
 
-// max over the two lanes that hold the same query (l and l ^ 32)
+// max / sum over the two lanes that hold the same query (l and l ^ 32)
 __device__ __forceinline__ float pair_max(float x) {
   const u32x2_t r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -95,7 +106,7 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kThreads, kQB == 1 ? 2 : 1) void attn_fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t ks[2 * kKTile];
   __shared__ __attribute__((aligned(16))) uint16_t vs[2 * kVTile];
 
@@ -106,19 +117,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   const int hf = lane >> 5;    // which 8-element half of a 16-deep k chunk
   const int nqb = (a.n + kBM - 1) / kBM;
   const int head = blockIdx.x / nqb;
-  const int qb = blockIdx.x - head * nqb;
-  const int qrow = qb * kBM + wave * 32 + col;
-  const bool qvalid = qrow < a.n;
+  const int qblk = blockIdx.x - head * nqb;
+  const float qscale = a.scale_log2;
 
-  // ---- Q~ fragment: B operand of S^T; lane holds dims 16c + 8hf .. +7 of its query
-  bf16x8_t qf[8];
-  {
-    const uint16_t* qp = a.q + (qvalid ? qrow : 0) * a.stride_qkv + head * kHeadDim + 8 * hf;
+  // ---- Q~ fragments: B operand of S^T; lane holds dims 16c + 8hf .. +7 of its query
+  int qrow[kQB];
+  bf16x8_t qf[kQB][8];
+#pragma unroll
+  for (int i = 0; i < kQB; ++i) {
+    qrow[i] = qblk * kBM + (wave * kQB + i) * 32 + col;
+    const bool qvalid = qrow[i] < a.n;
+    const uint16_t* qp = a.q + (qvalid ? qrow[i] : 0) * a.stride_qkv + head * kHeadDim + 8 * hf;
     float pos[3] = {0.0f, 0.0f, 0.0f};
     if (a.rope_q && qvalid) {
-      pos[0] = a.coords[3 * qrow + 0];
-      pos[1] = a.coords[3 * qrow + 1];
-      pos[2] = a.coords[3 * qrow + 2];
+      pos[0] = a.coords[3 * qrow[i] + 0];
+      pos[1] = a.coords[3 * qrow[i] + 1];
+      pos[2] = a.coords[3 * qrow[i] + 2];
     }
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
@@ -136,9 +150,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
         x = make_uint4(w[0], w[1], w[2], w[3]);
       }
       // pre-scale by scale * log2(e), rounding once more to bf16
-      x = make_uint4(scale_word(x.x, a.scale_log2), scale_word(x.y, a.scale_log2),
-                     scale_word(x.z, a.scale_log2), scale_word(x.w, a.scale_log2));
-      qf[c] = __builtin_bit_cast(bf16x8_t, x);
+      x = make_uint4(scale_word(x.x, qscale), scale_word(x.y, qscale), scale_word(x.z, qscale),
+                     scale_word(x.w, qscale));
+      qf[i][c] = __builtin_bit_cast(bf16x8_t, x);
     }
   }
 
@@ -160,31 +174,27 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   u32x4_t kr[kChunks], vr[kChunks];
   auto rsrc = [&](const char* base, int t) {
     const int64_t off = int64_t(t) * kBN * row_bytes;
-    // bytes left from this tile's first row; 0 past the end, so loads there read zeros
+    // bytes left from this tile's first row; the check on the tensor size keeps it below 2^32
     const int64_t left = span - off > 0 ? span - off : 0;
-    const int rec = static_cast<int>(static_cast<uint32_t>(left));   // < 2^32 by the size check
-    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + off), 0, rec, kRsrcFlags);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + off), 0, static_cast<int>(static_cast<uint32_t>(left)),
+                                             kRsrcFlags);
   };
-  auto load_k = [&](int t) {
-    const __amdgpu_buffer_rsrc_t d = rsrc(kbase, t);
+  auto load_tile = [&](int t) {
+    const __amdgpu_buffer_rsrc_t kd = rsrc(kbase, t);
+    const __amdgpu_buffer_rsrc_t vd = rsrc(vbase, t);
 #pragma unroll
     for (int r = 0; r < kChunks; ++r)
-      kr[r] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(d, voff[r], 0, 0));
-  };
-  auto load_v = [&](int t) {
-    const __amdgpu_buffer_rsrc_t d = rsrc(vbase, t);
+      kr[r] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(kd, voff[r], 0, 0));
 #pragma unroll
     for (int r = 0; r < kChunks; ++r)
-      vr[r] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(d, voff[r], 0, 0));
+      vr[r] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vd, voff[r], 0, 0));
   };
   lds_u16* ksl = (lds_u16*)ks;
   lds_u16* vsl = (lds_u16*)vs;
-  auto store_k = [&](int buf) {
+  auto store_tile = [&](int buf) {
 #pragma unroll
     for (int r = 0; r < kChunks; ++r)
       *reinterpret_cast<lds_u32x4*>(ksl + buf * kKTile + lds_k_st[r]) = kr[r];
-  };
-  auto store_v = [&](int buf) {
 #pragma unroll
     for (int r = 0; r < kChunks; ++r)
       *reinterpret_cast<lds_u32x4*>(vsl + buf * kVTile + lds_v_st[r]) = vr[r];
@@ -199,75 +209,68 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   const int g = lane >> 4;
   const int v_rd = (4 * (g >> 1) + ((lane >> 2) & 3)) * kVStr + 16 * (g & 1) + 4 * (lane & 3);
 
-  f32x16_t oacc[4];
+  f32x16_t oacc[kQB][4];
+  f32x16_t cinit[kQB];   // -m_ref in every entry: the start of each score chain
+  float m_ref[kQB];      // running reference max of the row, log2 units
+  float l_part[kQB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) oacc[i] = f32x16_t{};
-  float m_ref = 0.0f;          // running reference max of the row, log2 units
-  f32x16_t cinit = f32x16_t{}; // -m_ref in every entry: the start of each score chain
-  float l_part = 0.0f;
+  for (int i = 0; i < kQB; ++i) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) oacc[i][d] = f32x16_t{};
+    cinit[i] = f32x16_t{};
+    m_ref[i] = 0.0f;
+    l_part[i] = 0.0f;
+  }
   const bf16x2_t ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
-  // S^T = K~ Q~^T * scale * log2(e) - m for the two 32-key blocks of K buffer `buf`
-  auto scores = [&](int buf, f32x16_t& s0, f32x16_t& s1) {
+  // S^T (scaled, biased) for every query block and 32-key block of K buffer `buf`
+  auto scores = [&](int buf, f32x16_t (&s)[kQB][kKB]) {
     const lds_u16* kt = ksl + buf * kKTile + k_rd;
-    s0 = mfma32(*reinterpret_cast<const lds_bf16x8*>(kt), qf[0], cinit);
-    s1 = mfma32(*reinterpret_cast<const lds_bf16x8*>(kt + 32 * kKStr), qf[0], cinit);
 #pragma unroll
-    for (int c = 1; c < 8; ++c) {
-      const bf16x8_t k0 = *reinterpret_cast<const lds_bf16x8*>(kt + 16 * c);
-      const bf16x8_t k1 = *reinterpret_cast<const lds_bf16x8*>(kt + 32 * kKStr + 16 * c);
-      s0 = mfma32(k0, qf[c], s0);
-      s1 = mfma32(k1, qf[c], s1);
+    for (int b = 0; b < kKB; ++b) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const bf16x8_t kop = *reinterpret_cast<const lds_bf16x8*>(kt + 32 * b * kKStr + 16 * c);
+#pragma unroll
+        for (int i = 0; i < kQB; ++i) s[i][b] = mfma32(kop, qf[i][c], c == 0 ? cinit[i] : s[i][b]);
+      }
     }
   };
 
   // P = exp2(S) as bf16 (pb[b][half] is the B operand of PV chunk 2b + half);
-  // returns this lane's sum of the tile's P
-  auto probs = [&](const f32x16_t& s0, const f32x16_t& s1, bf16x8_t (&pb)[2][2]) {
+  // returns this lane's sum of the block's P
+  auto probs = [&](const f32x16_t (&s)[kKB], bf16x8_t (&pb)[kKB][2]) {
     float lt = 0.0f;
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      bf16x2_t p0, p1;
-      p0[0] = static_cast<__bf16>(__builtin_amdgcn_exp2f(s0[r]));
-      p0[1] = static_cast<__bf16>(__builtin_amdgcn_exp2f(s0[r + 1]));
-      p1[0] = static_cast<__bf16>(__builtin_amdgcn_exp2f(s1[r]));
-      p1[1] = static_cast<__bf16>(__builtin_amdgcn_exp2f(s1[r + 1]));
-      lt = __builtin_amdgcn_fdot2_f32_bf16(p0, ones, lt, false);
-      lt = __builtin_amdgcn_fdot2_f32_bf16(p1, ones, lt, false);
-      pb[0][r >> 3][r & 7] = p0[0];
-      pb[0][r >> 3][(r & 7) + 1] = p0[1];
-      pb[1][r >> 3][r & 7] = p1[0];
-      pb[1][r >> 3][(r & 7) + 1] = p1[1];
-    }
+    for (int b = 0; b < kKB; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        bf16x2_t p;
+        p[0] = static_cast<__bf16>(__builtin_amdgcn_exp2f(s[b][r]));
+        p[1] = static_cast<__bf16>(__builtin_amdgcn_exp2f(s[b][r + 1]));
+        lt = __builtin_amdgcn_fdot2_f32_bf16(p, ones, lt, false);
+        pb[b][r >> 3][r & 7] = p[0];
+        pb[b][r >> 3][(r & 7) + 1] = p[1];
+      }
     return lt;
   };
 
-  // row max of a tile over both lanes of each query
-  auto tile_max = [&](const f32x16_t& s0, const f32x16_t& s1) {
+  // row max of one query block's tile over both lanes of each query
+  auto tile_max = [&](const f32x16_t (&s)[kKB]) {
     // NaN-propagating maximum: lowers to v_maximum3_f32 with no input canonicalisation
-    float mt = __builtin_elementwise_maximum(s0[0], s1[0]);
+    float mt = s[0][0];
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mt = __builtin_elementwise_maximum(mt, __builtin_elementwise_maximum(s0[r], s1[r]));
+    for (int b = 0; b < kKB; ++b)
+#pragma unroll
+      for (int r = (b == 0 ? 1 : 0); r < 16; ++r) mt = __builtin_elementwise_maximum(mt, s[b][r]);
     return pair_max(mt);
   };
 
-  // raise the reference by delta >= 0: shift the live scores, rescale O and l
-  auto raise_ref = [&](float delta, f32x16_t& s0, f32x16_t& s1) {
-    s0 -= delta;
-    s1 -= delta;
-    cinit -= delta;
-    m_ref += delta;
-    const float alpha = __builtin_amdgcn_exp2f(-delta);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) oacc[i] *= alpha;
-    l_part *= alpha;
-  };
-
-  // O^T += V^T P^T over four 16-key chunks and four 32-dim blocks of V buffer `buf`
-  auto pv = [&](int buf, const bf16x8_t (&pb)[2][2]) {
+  // O^T += V^T P^T over the tile's 16-key chunks and four 32-dim blocks of V buffer `buf`
+  auto pv = [&](int buf, const bf16x8_t (&pb)[kQB][kKB][2]) {
     const lds_u16* vt = vsl + buf * kVTile + v_rd;
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
+    for (int kc = 0; kc < 2 * kKB; ++kc) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -275,47 +278,72 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
         const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             reinterpret_cast<lds_i16x4*>(const_cast<lds_u16*>(vt + (16 * kc + 8) * kVStr + 32 * db)));
         const i16x4_t both[2] = {lo, hi};
-        oacc[db] = mfma32(__builtin_bit_cast(bf16x8_t, both), pb[kc >> 1][kc & 1], oacc[db]);
+        const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, both);
+#pragma unroll
+        for (int i = 0; i < kQB; ++i) oacc[i][db] = mfma32(vop, pb[i][kc >> 1][kc & 1], oacc[i][db]);
       }
     }
   };
 
   // keys past the end of the sequence take no weight (last tile only)
-  auto mask_tail = [&](f32x16_t& s0, f32x16_t& s1, int key0) {
+  auto mask_tail = [&](f32x16_t (&s)[kQB][kKB], int key0) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = key0 + 8 * (r >> 2) + 4 * hf + (r & 3);
-      if (key >= a.n) s0[r] = -__builtin_inff();
-      if (key + 32 >= a.n) s1[r] = -__builtin_inff();
-    }
+    for (int b = 0; b < kKB; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + 32 * b + 8 * (r >> 2) + 4 * hf + (r & 3);
+        if (key >= a.n) {
+#pragma unroll
+          for (int i = 0; i < kQB; ++i) s[i][b][r] = -__builtin_inff();
+        }
+      }
   };
 
   // One tile: scores, softmax, PV.  The first tile sets the reference max (O and
   // l are still zero); the last one masks keys >= n.
   auto step = [&](int t, auto first, auto last) {
-    f32x16_t s0, s1;
-    scores(t & 1, s0, s1);
-    if constexpr (decltype(last)::value) mask_tail(s0, s1, t * kBN);
+    f32x16_t s[kQB][kKB];
+    scores(t & 1, s);
+    if constexpr (decltype(last)::value) mask_tail(s, t * kBN);
     if constexpr (decltype(first)::value) {
-      const float mt = tile_max(s0, s1);
-      s0 -= mt;
-      s1 -= mt;
-      cinit -= mt;
-      m_ref = mt;
-    }
-    bf16x8_t pb[2][2];
-    float lt = probs(s0, s1, pb);
-    if constexpr (!decltype(first)::value) {
-      if (__builtin_amdgcn_ballot_w64(lt > kMaxTileSum) != 0) {
-        raise_ref(__builtin_elementwise_maximum(tile_max(s0, s1), 0.0f), s0, s1);
-        lt = probs(s0, s1, pb);
+#pragma unroll
+      for (int i = 0; i < kQB; ++i) {
+        const float mt = tile_max(s[i]);
+#pragma unroll
+        for (int b = 0; b < kKB; ++b) s[i][b] -= mt;
+        cinit[i] -= mt;
+        m_ref[i] = mt;
       }
     }
-    l_part += lt;
+    bf16x8_t pb[kQB][kKB][2];
+    float lt[kQB];
+#pragma unroll
+    for (int i = 0; i < kQB; ++i) lt[i] = probs(s[i], pb[i]);
+    if constexpr (!decltype(first)::value) {
+      bool big = false;
+#pragma unroll
+      for (int i = 0; i < kQB; ++i) big = big || lt[i] > kMaxTileSum;
+      if (__builtin_amdgcn_ballot_w64(big) != 0) {
+        // raise each reference by the tile's excess (never lower it), rescale, redo the tile
+#pragma unroll
+        for (int i = 0; i < kQB; ++i) {
+          const float delta = __builtin_elementwise_maximum(tile_max(s[i]), 0.0f);
+#pragma unroll
+          for (int b = 0; b < kKB; ++b) s[i][b] -= delta;
+          cinit[i] -= delta;
+          m_ref[i] += delta;
+          const float alpha = __builtin_amdgcn_exp2f(-delta);
+#pragma unroll
+          for (int d = 0; d < 4; ++d) oacc[i][d] *= alpha;
+          l_part[i] *= alpha;
+          lt[i] = probs(s[i], pb[i]);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kQB; ++i) l_part[i] += lt[i];
     pv(t & 1, pb);
   };
-  auto load_tile = [&](int t) { load_k(t); load_v(t); };
-  auto store_tile = [&](int buf) { store_k(buf); store_v(buf); };
 
   // Double-buffered tiles, one barrier per tile: tile t+1 is loaded into
   // registers while tile t is computed, then stored into the other buffer.
@@ -339,22 +367,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
     step(ntiles - 1, False{}, True{});
   }
 
-  // ---- epilogue: O = O^T / l, LSE = m * scale + ln l
-  const float l_tot = pair_sum(l_part);
-  if (qvalid) {
-    const float inv = 1.0f / l_tot;
-    uint16_t* op = a.o + qrow * a.stride_o + head * kHeadDim;
+  // ---- epilogue: O = O^T / l, LSE = (m + log2 l) * ln 2
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+  for (int i = 0; i < kQB; ++i) {
+    const float l_tot = pair_sum(l_part[i]);
+    if (qrow[i] < a.n) {
+      const float inv = 1.0f / l_tot;
+      uint16_t* op = a.o + qrow[i] * a.stride_o + head * kHeadDim;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d = 32 * db + 8 * i + 4 * hf;
-        const uint2 w = make_uint2(pack_bf16x2(oacc[db][4 * i + 0] * inv, oacc[db][4 * i + 1] * inv),
-                                   pack_bf16x2(oacc[db][4 * i + 2] * inv, oacc[db][4 * i + 3] * inv));
-        *reinterpret_cast<uint2*>(op + d) = w;
-      }
-    // m_ref is in log2 units of the scaled scores: LSE = (m_ref + log2 l) * ln 2
-    if (a.lse != nullptr && hf == 0) a.lse[head * a.n + qrow] = (m_ref + __log2f(l_tot)) * 0.69314718055994531f;
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int d = 32 * db + 8 * r + 4 * hf;
+          const uint2 w = make_uint2(pack_bf16x2(oacc[i][db][4 * r + 0] * inv, oacc[i][db][4 * r + 1] * inv),
+                                     pack_bf16x2(oacc[i][db][4 * r + 2] * inv, oacc[i][db][4 * r + 3] * inv));
+          *reinterpret_cast<uint2*>(op + d) = w;
+        }
+      if (a.lse != nullptr && hf == 0)
+        a.lse[head * a.n + qrow[i]] = (m_ref[i] + __log2f(l_tot)) * 0.69314718055994531f;
+    }
   }
 }
 
