@@ -226,15 +226,18 @@ __global__ __launch_bounds__(kThreads, kQB == 1 ? 2 : 1) void attn_fwd_kernel(Fw
   // S^T (scaled, biased) for every query block and 32-key block of K buffer `buf`
   auto scores = [&](int buf, f32x16_t (&s)[kQB][kKB]) {
     const lds_u16* kt = ksl + buf * kKTile + k_rd;
+    // all K operands of the tile first, so the LDS reads overlap the MFMA chains
+    bf16x8_t kop[kKB][8];
 #pragma unroll
-    for (int b = 0; b < kKB; ++b) {
+    for (int c = 0; c < 8; ++c)
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const bf16x8_t kop = *reinterpret_cast<const lds_bf16x8*>(kt + 32 * b * kKStr + 16 * c);
+      for (int b = 0; b < kKB; ++b) kop[b][c] = *reinterpret_cast<const lds_bf16x8*>(kt + 32 * b * kKStr + 16 * c);
 #pragma unroll
-        for (int i = 0; i < kQB; ++i) s[i][b] = mfma32(kop, qf[i][c], c == 0 ? cinit[i] : s[i][b]);
-      }
-    }
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int b = 0; b < kKB; ++b)
+#pragma unroll
+        for (int i = 0; i < kQB; ++i) s[i][b] = mfma32(kop[b][c], qf[i][c], c == 0 ? cinit[i] : s[i][b]);
   };
 
   // P = exp2(S) as bf16 (pb[b][half] is the B operand of PV chunk 2b + half);

@@ -5,8 +5,8 @@
 // together", position-chain paragraph): coordinates (t, h, w) -> rope() ->
 // rotate Q and K.  The head dim is split into contiguous t | h | w sections;
 // inside section a, pair p turns dims (o_a + 2p, o_a + 2p + 1) by
-// pos_a * theta_a^(-2p / d_a).  The angle and its cos / sin are formed in
-// binary64 and rounded to binary32; the rotation runs in binary32 with explicit
+// pos_a * theta_a^(-2p / d_a).  The angle is formed and reduced in binary64,
+// its cos / sin taken in binary32; the rotation runs in binary32 with explicit
 // fused multiply-adds and the result is rounded to bfloat16, nearest even.
 #pragma once
 
@@ -30,13 +30,15 @@ __device__ __forceinline__ int rope_axis(int pair, const RopeTable& tab) {
   return (pair >= tab.b1) + (pair >= tab.b2);
 }
 
-// cos / sin of the angle of `pair` for a row at position pos.
+// cos / sin of the angle pos * freq.  The angle is formed and reduced modulo
+// 2 pi in binary64 (the reduction error is k * 2.4e-16 for k turns, far below
+// binary32 resolution at any exact coordinate), then the binary32 sincos of the
+// remainder in [-pi, pi] is taken.
 __device__ __forceinline__ void rope_cos_sin(float pos, double freq, float& c, float& s) {
   const double ang = static_cast<double>(pos) * freq;
-  double sd, cd;
-  sincos(ang, &sd, &cd);
-  c = static_cast<float>(cd);
-  s = static_cast<float>(sd);
+  const double turns = __builtin_rint(ang * 0.15915494309189535);       // round(ang / (2 pi))
+  const float r = static_cast<float>(__builtin_fma(-turns, 6.283185307179586, ang));
+  sincosf(r, &s, &c);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {

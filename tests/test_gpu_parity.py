@@ -11,10 +11,11 @@ the binade), so each score s = q.k / sqrt(D) moves by sigma_s ~ sqrt(2) * 1.7e-3
 ~ 2.4e-3 for unit-variance inputs.  LSE is a weighted mean of score moves; a
 row dominated by one key follows that key's move, so 1e-2 (about 4 sigma_s) is
 the worst case for these workloads, whose rows are not peaked.
-RoPE pass: the kernel forms cos/sin from a binary64 angle and rotates in
-binary32, so before its final bf16 rounding it is within ~1e-6 of the pair
-norm of the exact value; after rounding each element is within half a bf16
-ulp of that, i.e. |gpu - exact| <= 0.5 ulp(|exact| + e) + e, e = 1e-6 * |pair|.
+RoPE pass: the kernel forms the angle in binary64, reduces it modulo 2 pi,
+takes binary32 cos/sin of the remainder (error ~1e-7) and rotates in binary32,
+so before its final bf16 rounding it is within ~1e-6 of the pair norm of the
+exact value; after rounding each element is within half a bf16 ulp of that,
+i.e. |gpu - exact| <= 0.5 ulp(|exact| + e) + e, e = 1e-6 * |pair|.
 """
 import numpy as np
 import pytest
