@@ -9,7 +9,10 @@ statement of what the hot path computes, written from the pages:
 * "MiniMax H3 - one transformer that denoises video and audio together"
   (paragraphs on latent frames, the 40 Hz clock and the 5/3 frame rescale,
   text as 1-D RoPE, the position chain into rope(), the normalised spatial grid),
-* "MiniMax Opens H3 Base Weights ..." (full attention only in the open release).
+* "MiniMax Opens H3 Base Weights ..." (full attention only in the open release),
+* AdaLN: the AdaLN paragraphs of the explainer page (norm(x) * (1 + scale) +
+  shift, index = timestep_index * 3 + token_tag) and section 5 of the thread
+  (shift, scale and gate per block for the attention and MLP paths).
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import it.  It shares no code with the HIP library and imports
@@ -19,10 +22,12 @@ Modules:
   coords     - segment table -> (t, h, w) per row, float32, exact rounding
   rope       - three-axis rotary embedding of Q / K, float64
   attention  - softmax(QK^T * scale) V per head, float64, plus log-sum-exp
+  adaln      - per-row indexed modulation, the gated residual, float64
 """
 from .coords import build_coords, f32_round, video_hw_f64
 from .rope import inv_freq, rope
 from .attention import attention, bf16_bits_to_f64
+from . import adaln
 
 __all__ = ["build_coords", "f32_round", "video_hw_f64", "inv_freq", "rope",
-           "attention", "bf16_bits_to_f64"]
+           "attention", "bf16_bits_to_f64", "adaln"]

@@ -108,3 +108,36 @@ def qkv(n, h, seed=DEFAULT_SEED, d=HEAD_DIM, q_scale=1.0):
     k = normal_bf16((n, h, d), seed + 1)
     v = normal_bf16((n, h, d), seed + 2)
     return q, k, v
+
+
+# ---- AdaLN modulation inputs (hidden size and per-row table selectors)
+ADALN_HIDDEN = 5376   # 42 heads x 128
+ADALN_PARAMS = 6      # per table entry: shift, scale, gate of the attention path, then of the MLP path
+
+
+def adaln_rows(segments):
+    """Per-row (timestep index, token tag) of a packed sequence, in row order.
+
+    tag: the segment kind (0 text, 1 video, 2 audio).  Timestep index 0 is the
+    denoising step of the target rows; text rows take the same index (text
+    inherits the video timestep).  Media segments that start before t = 0 are
+    references (clean context) and take index 1.
+    """
+    t_idx, tags = [], []
+    for s in segments:
+        rows = s.frames * s.grid_h * s.grid_w
+        ref = s.kind != TEXT and s.t0_thirds < 0
+        t_idx.append(np.full(rows, 1 if ref else 0, np.int32))
+        tags.append(np.full(rows, s.kind, np.int32))
+    if not t_idx:
+        return np.zeros(0, np.int32), np.zeros(0, np.int32)
+    return np.concatenate(t_idx), np.concatenate(tags)
+
+
+def adaln_inputs(n, c=ADALN_HIDDEN, n_timesteps=2, seed=DEFAULT_SEED, table_scale=0.5):
+    """Residual stream x, sublayer output y (bf16 bits [n, c]) and the modulation
+    table (bf16 bits [n_timesteps * 3, 6, c]); seeds seed+10, +11, +12."""
+    x = normal_bf16((n, c), seed + 10)
+    y = normal_bf16((n, c), seed + 11)
+    table = normal_bf16((n_timesteps * 3, ADALN_PARAMS, c), seed + 12, table_scale)
+    return x, y, table
