@@ -8,6 +8,12 @@ Inputs are seeded synthetic bf16 N(0, 1) tensors, resident in HBM before the
 timed region.  Prints one JSON line.
 
 FLOP counted per step: 4 N^2 H D (the two products of full attention).
+
+--path adaln times the AdaLN row instead: one h3attn_adaln_residual call (the
+gated residual of a sublayer fused with the next modulated layer norm) over
+the same 28,192 rows x 5,376 hidden, per-row table entries timestep * 3 + tag;
+bytes counted per step: x, y read, x_out, h written (2 B each per element),
+the int32 selectors and the three table planes once.
 """
 import argparse
 import json
@@ -23,24 +29,28 @@ import numpy as np  # noqa: E402
 import workloads as W  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
-ATTN_SOURCE = os.path.join(ROOT, "stream_audio_video_amd", "csrc", "attn_fwd.hip")
+PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+CSRC = os.path.join(ROOT, "stream_audio_video_amd", "csrc")
+ATTN_SOURCE = os.path.join(CSRC, "attn_fwd.hip")
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "attn_fwd_5s_hbm_traffic.json")
+ADALN_SOURCE = os.path.join(CSRC, "adaln_kernel.hip")
+ADALN_TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "adaln_residual_5s_hbm_traffic.json")
 
 
-def measured_traffic():
-    """HBM bytes per attention launch from the committed counter record, or None.
+def measured_traffic(record=TRAFFIC_RECORD, source=ATTN_SOURCE, key="attn_fwd_sha256"):
+    """HBM bytes per launch from a committed counter record, or None.
 
     The record holds FETCH_SIZE / WRITE_SIZE per dispatch already scaled by the
-    copy-kernel calibration; it is used only while the attention source still has
+    copy-kernel calibration; it is used only while the kernel source still has
     the hash the counters were taken with.
     """
     import hashlib
     try:
-        rec = json.load(open(TRAFFIC_RECORD))
-        digest = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()
+        rec = json.load(open(record))
+        digest = hashlib.sha256(open(source, "rb").read()).hexdigest()
     except (OSError, ValueError):
         return None
-    if rec.get("attn_fwd_sha256") != digest:
+    if rec.get(key) != digest:
         return None
     return rec.get("bytes_per_launch")
 METRIC = "MM-RoPE+attention TFLOP/s & % bf16 MFMA peak, 28,192-token packed seq"
@@ -75,6 +85,89 @@ def cpu_baseline(name, q, k, v, segs, budget_s):
                       "%.1f s of fp64 numpy; FLOP 4*rows*N*D" % (name, rows_done - 1, n, t_used)}
 
 
+ADALN_METRIC = "AdaLN gated residual + modulated layer norm GB/s & % HBM peak, 28,192 rows x 5,376"
+
+
+def adaln_bytes(n, c, n_entries):
+    return 4 * n * c * 2 + 8 * n + 3 * n_entries * c * 2
+
+
+def adaln_cpu_baseline(x, y, table, t_idx, tags, budget_s):
+    """Time the fp64 oracle of the gated residual + modulated norm on rows in blocks of 256, ~budget_s."""
+    from oracle import adaln as A
+    n, c = x.shape
+    tab = A.bf16_bits_to_f64(table)
+    idx_all = A.adaln_index(t_idx, tags)
+    rows_done, t_used = 0, 0.0
+    while t_used < budget_s and rows_done < n:
+        r = slice(rows_done, min(n, rows_done + 256))
+        xb, yb = A.bf16_bits_to_f64(x[r]), A.bf16_bits_to_f64(y[r])
+        t0 = time.perf_counter()
+        A.residual_modulate(xb, yb, idx_all[r], tab[:, 2], tab[:, 3], tab[:, 4], A.LAYER_NORM, 1e-6)
+        t_used += time.perf_counter() - t0
+        rows_done = r.stop
+    nbytes = 4 * rows_done * c * 2 + 8 * rows_done
+    return {"value": nbytes / t_used / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "rows 0..%d of %d (blocks of 256), %.1f s of fp64 numpy; bytes 8*rows*C + 8*rows"
+                      % (rows_done - 1, n, t_used)}
+
+
+def bench_adaln(args):
+    import torch
+    import stream_audio_video_amd as h3
+    h3.load_library()
+    dev = torch.device("cuda:0")
+    _, segs = W.CONFIGS[args.config]
+    n, c = W.n_tokens(segs), W.ADALN_HIDDEN
+    x, y, table = W.adaln_inputs(n, c)
+    t_idx, tags = W.adaln_rows(segs)
+    to_dev = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)
+    xd, yd, tab = to_dev(x), to_dev(y), to_dev(table)
+    ti, tg = torch.from_numpy(t_idx).to(dev), torch.from_numpy(tags).to(dev)
+    xo, hd = torch.empty_like(xd), torch.empty_like(xd)
+    base, ne = tab.data_ptr(), table.shape[0]
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        h3.adaln_residual(xd, yd, c, ti, tg, base + 2 * 2 * c, base + 3 * 2 * c, base + 4 * 2 * c, 6 * c, ne,
+                          xo, hd, c, n, c, h3.LAYER_NORM, 1e-6)
+        if ev is not None:
+            ev[1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    k_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    nbytes = adaln_bytes(n, c, ne)
+    value = nbytes / (ms_step * 1e-3) / 1e9
+    achieved = nbytes / (k_ms * 1e-3) / 1e9
+    cpu = adaln_cpu_baseline(x, y, table, t_idx, tags, args.cpu_budget) if args.cpu_budget > 0 else None
+    rec = {
+        "metric": ADALN_METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "%s packed sequence, %d rows x %d hidden, %d table entries (2 timesteps x 3 tags)"
+                               % (args.config, n, c, ne),
+                   "rows": n, "hidden": c, "norm": "layer", "kernel_ms": round(k_ms, 4),
+                   "bytes_per_step": nbytes},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": measured_traffic(ADALN_TRAFFIC_RECORD, ADALN_SOURCE, "adaln_sha256")},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -82,6 +175,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="5s", choices=list(W.CONFIGS))
     ap.add_argument("--mode", default="fused", choices=["fused", "prerotated"])
+    ap.add_argument("--path", default="attention", choices=["attention", "adaln"],
+                    help="attention: MM-RoPE + attention (the headline); adaln: the AdaLN residual row")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing (0 = skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB MiB three times (scales HBM byte counters)")
@@ -99,6 +194,9 @@ def main():
     if args.gpus != 1:
         print("bench.py measures one GPU only: the path is single-GPU (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    if args.path == "adaln":
+        bench_adaln(args)
+        return
 
     import torch
     import stream_audio_video_amd as h3

@@ -143,10 +143,70 @@ int h3attn_forward(const h3attn_rope_cfg* cfg, const float* coords_dev, int32_t 
                    int64_t n_tokens, int32_t n_heads, int64_t row_stride_qkv,
                    int64_t row_stride_o, float scale, void* stream);
 
+/*
+ * ---- Indexed AdaLN modulation around attention ----
+ *
+ * Sources: "MiniMax H3 - one transformer that denoises video and audio
+ * together", AdaLN paragraphs (a sublayer input becomes norm(x) * (1 + scale) +
+ * shift; H3 keeps a table indexed by (noise level, modality) and every row looks
+ * up entry timestep_index * 3 + token_tag); "Inside MiniMax H3: One DiT Stream
+ * for Text, Video, and Stereo Audio", section 5 (each block produces shift,
+ * scale and gate for its attention and MLP paths, gathered per row).
+ *
+ * Readings where the pages are silent: norm is a layer norm without affine
+ * ((x - mean) / sqrt(var + eps), biased variance over the row) or, on request, a
+ * root-mean-square norm (x / sqrt(mean(x^2) + eps)); a gate scales the sublayer
+ * output before it joins the residual stream (x + gate * y); token tags are
+ * 0 text, 1 video, 2 audio.
+ *
+ * Conventions of both calls:
+ *   x, y, h, x_out   bf16, row-major [n_rows][stride], 16-byte aligned, stride in
+ *                    elements (>= hidden, multiple of 8)
+ *   t_idx, tags      device int32 [n_rows]: entry e = t_idx * 3 + tags
+ *   gate/shift/scale device bf16 table planes: entry e starts at plane + e * entry_stride
+ *                    elements (for an [E][6][hidden] table in the order
+ *                    shift_attn, scale_attn, gate_attn, shift_mlp, scale_mlp, gate_mlp,
+ *                    pass table + k * hidden and entry_stride = 6 * hidden)
+ *   n_entries        entries in the table (> 0)
+ *   hidden           8 <= hidden <= H3ATTN_ADALN_MAX_HIDDEN, multiple of 8 (5,376 here)
+ *   norm_kind        H3ATTN_LAYER_NORM or H3ATTN_RMS_NORM;  eps >= 0
+ * Arithmetic is float32, each output rounded once to bf16 (nearest even).  A row
+ * whose t_idx < 0, tag outside [0, 3) or entry >= n_entries reads no table entry;
+ * its outputs are written as bf16 NaN.  n_rows == 0 is a no-op.  Errors: EINVAL
+ * (sizes, alignment, overlaps, null pointers), ERANGE (n_rows >= 2^31),
+ * EUNSUPPORTED, EHIP.
+ */
+#define H3ATTN_ADALN_MAX_HIDDEN 8192
+enum { H3ATTN_LAYER_NORM = 0, H3ATTN_RMS_NORM = 1 };
+
+/*
+ * Device call.  h = norm(x) * (1 + scale[e]) + shift[e] per row (the modulated
+ * input of a sublayer).  h may be x itself (in place); otherwise they must not
+ * overlap.
+ */
+int h3attn_adaln_modulate(const void* x, int64_t x_stride, const int32_t* t_idx, const int32_t* tags,
+                          const void* shift, const void* scale, int64_t entry_stride, int32_t n_entries,
+                          void* h, int64_t h_stride, int64_t n_rows, int32_t hidden,
+                          int32_t norm_kind, float eps, void* stream);
+
+/*
+ * Device call.  The gated residual of one sublayer fused with the modulated
+ * norm of the next:
+ *   x_out = bf16(x + gate[e] * y)
+ *   h     = norm(x_out) * (1 + scale[e]) + shift[e]      (norm of the stored bf16 row)
+ * x and y share xy_stride; x_out and h share out_stride.  x_out may be x itself
+ * (in place, then out_stride == xy_stride); no other buffers may overlap.
+ */
+int h3attn_adaln_residual(const void* x, const void* y, int64_t xy_stride, const int32_t* t_idx,
+                          const int32_t* tags, const void* gate, const void* shift, const void* scale,
+                          int64_t entry_stride, int32_t n_entries, void* x_out, void* h,
+                          int64_t out_stride, int64_t n_rows, int32_t hidden, int32_t norm_kind,
+                          float eps, void* stream);
+
 /* Static description of an error code (never NULL). */
 const char* h3attn_strerror(int code);
 
-/* Library version string, e.g. "h3attn 0.1.0 gfx950". */
+/* Library version string, e.g. "h3attn 0.2.0 gfx950". */
 const char* h3attn_version(void);
 
 #ifdef __cplusplus

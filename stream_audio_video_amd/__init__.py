@@ -8,6 +8,10 @@ device memory and the current stream.  The functions keep the C names:
   rope_qk(cfg, coords_dev, q_in, q_out, k_in, k_out, n_tokens, n_heads, row_stride, stream=None)
   forward(cfg, coords_dev, rope_q, q, k, v, o, lse, n_tokens, n_heads,
           row_stride_qkv, row_stride_o, scale=0.0, stream=None)
+  adaln_modulate(x, x_stride, t_idx, tags, shift, scale, entry_stride, n_entries, h, h_stride,
+                 n_rows, hidden, norm_kind=LAYER_NORM, eps=1e-6, stream=None)
+  adaln_residual(x, y, xy_stride, t_idx, tags, gate, shift, scale, entry_stride, n_entries,
+                 x_out, h, out_stride, n_rows, hidden, norm_kind=LAYER_NORM, eps=1e-6, stream=None)
   strerror(code), version()
 
 Tensor arguments may be torch tensors (their data_ptr is passed) or raw
@@ -23,9 +27,11 @@ _lib = None
 
 H3ATTN_OK, H3ATTN_EINVAL, H3ATTN_ERANGE, H3ATTN_EUNSUPPORTED, H3ATTN_EHIP = 0, -1, -2, -3, -4
 SEG_TEXT, SEG_VIDEO, SEG_AUDIO = 0, 1, 2
+LAYER_NORM, RMS_NORM = 0, 1
+ADALN_MAX_HIDDEN = 8192
 
-EXPORTED = ("h3attn_build_coords", "h3attn_rope_qk", "h3attn_forward", "h3attn_strerror",
-            "h3attn_version")
+EXPORTED = ("h3attn_build_coords", "h3attn_rope_qk", "h3attn_forward", "h3attn_adaln_modulate",
+            "h3attn_adaln_residual", "h3attn_strerror", "h3attn_version")
 
 
 class H3AttnError(RuntimeError):
@@ -65,6 +71,12 @@ def load_library(path=None):
     lib.h3attn_forward.argtypes = [ctypes.POINTER(RopeCfg), vp, i32, vp, vp, vp, vp, vp, i64, i32, i64, i64,
                                    ctypes.c_float, vp]
     lib.h3attn_forward.restype = ctypes.c_int
+    lib.h3attn_adaln_modulate.argtypes = [vp, i64, vp, vp, vp, vp, i64, i32, vp, i64, i64, i32, i32,
+                                          ctypes.c_float, vp]
+    lib.h3attn_adaln_modulate.restype = ctypes.c_int
+    lib.h3attn_adaln_residual.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp, i64, i32, vp, vp, i64, i64, i32, i32,
+                                          ctypes.c_float, vp]
+    lib.h3attn_adaln_residual.restype = ctypes.c_int
     lib.h3attn_strerror.argtypes = [ctypes.c_int]
     lib.h3attn_strerror.restype = ctypes.c_char_p
     lib.h3attn_version.argtypes = []
@@ -141,6 +153,25 @@ def forward(cfg, coords_dev, rope_q, q, k, v, o, lse, n_tokens, n_heads, row_str
                              int(row_stride_o), float(scale), _stream(stream))
     if rc != H3ATTN_OK:
         raise H3AttnError("h3attn_forward", rc)
+
+
+def adaln_modulate(x, x_stride, t_idx, tags, shift, scale, entry_stride, n_entries, h, h_stride, n_rows,
+                   hidden, norm_kind=LAYER_NORM, eps=1e-6, stream=None):
+    rc = _L().h3attn_adaln_modulate(_ptr(x), int(x_stride), _ptr(t_idx), _ptr(tags), _ptr(shift), _ptr(scale),
+                                    int(entry_stride), int(n_entries), _ptr(h), int(h_stride), int(n_rows),
+                                    int(hidden), int(norm_kind), float(eps), _stream(stream))
+    if rc != H3ATTN_OK:
+        raise H3AttnError("h3attn_adaln_modulate", rc)
+
+
+def adaln_residual(x, y, xy_stride, t_idx, tags, gate, shift, scale, entry_stride, n_entries, x_out, h,
+                   out_stride, n_rows, hidden, norm_kind=LAYER_NORM, eps=1e-6, stream=None):
+    rc = _L().h3attn_adaln_residual(_ptr(x), _ptr(y), int(xy_stride), _ptr(t_idx), _ptr(tags), _ptr(gate),
+                                    _ptr(shift), _ptr(scale), int(entry_stride), int(n_entries), _ptr(x_out),
+                                    _ptr(h), int(out_stride), int(n_rows), int(hidden), int(norm_kind),
+                                    float(eps), _stream(stream))
+    if rc != H3ATTN_OK:
+        raise H3AttnError("h3attn_adaln_residual", rc)
 
 
 def mmrope_attention(q, k, v, coords_dev, cfg=None, scale=0.0, want_lse=True, fuse_q=True, k_rot=None,

@@ -139,6 +139,93 @@ extern "C" int h3attn_forward(const h3attn_rope_cfg* cfg, const float* coords_de
                                                                                 : H3ATTN_EHIP;
 }
 
+namespace {
+
+// Shared checks of the two AdaLN entry points; fills everything but y / gate / x_out.
+int adaln_common(const void* x, int64_t x_stride, const int32_t* t_idx, const int32_t* tags,
+                 const void* shift, const void* scale, int64_t entry_stride, int32_t n_entries, void* h,
+                 int64_t h_stride, int64_t n_rows, int32_t hidden, int32_t norm_kind, float eps,
+                 h3::AdalnArgs* a) {
+  if (n_rows < 0 || n_rows >= (int64_t(1) << 31)) return n_rows < 0 ? H3ATTN_EINVAL : H3ATTN_ERANGE;
+  if (hidden < 8 || hidden > H3ATTN_ADALN_MAX_HIDDEN || (hidden & 7) != 0) return H3ATTN_EINVAL;
+  if (norm_kind != H3ATTN_LAYER_NORM && norm_kind != H3ATTN_RMS_NORM) return H3ATTN_EINVAL;
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return H3ATTN_EINVAL;
+  if (n_entries <= 0 || entry_stride < 0 || (entry_stride & 7) != 0) return H3ATTN_EINVAL;
+  if (x_stride < hidden || (x_stride & 7) != 0 || h_stride < hidden || (h_stride & 7) != 0) return H3ATTN_EINVAL;
+  if (x == nullptr || h == nullptr || t_idx == nullptr || tags == nullptr || shift == nullptr || scale == nullptr)
+    return H3ATTN_EINVAL;
+  for (const void* p : {x, static_cast<const void*>(h), shift, scale})
+    if (!aligned16(p)) return H3ATTN_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(t_idx) & 3u) != 0 || (reinterpret_cast<uintptr_t>(tags) & 3u) != 0)
+    return H3ATTN_EINVAL;
+  a->x = static_cast<const uint16_t*>(x);
+  a->t_idx = t_idx;
+  a->tags = tags;
+  a->shift = static_cast<const uint16_t*>(shift);
+  a->scale = static_cast<const uint16_t*>(scale);
+  a->h = static_cast<uint16_t*>(h);
+  a->x_stride = x_stride;
+  a->h_stride = h_stride;
+  a->entry_stride = entry_stride;
+  a->n_entries = n_entries;
+  a->n_rows = n_rows;
+  a->hidden = hidden;
+  a->norm_kind = norm_kind;
+  a->eps = eps;
+  return H3ATTN_OK;
+}
+
+int64_t span_bytes(int64_t rows, int64_t stride, int64_t width) { return ((rows - 1) * stride + width) * 2; }
+
+}  // namespace
+
+extern "C" int h3attn_adaln_modulate(const void* x, int64_t x_stride, const int32_t* t_idx, const int32_t* tags,
+                                     const void* shift, const void* scale, int64_t entry_stride,
+                                     int32_t n_entries, void* h, int64_t h_stride, int64_t n_rows,
+                                     int32_t hidden, int32_t norm_kind, float eps, void* stream) {
+  h3::AdalnArgs a;
+  std::memset(&a, 0, sizeof(a));
+  int rc = adaln_common(x, x_stride, t_idx, tags, shift, scale, entry_stride, n_entries, h, h_stride, n_rows,
+                        hidden, norm_kind, eps, &a);
+  if (rc != H3ATTN_OK) return rc;
+  if (n_rows == 0) return H3ATTN_OK;
+  // h may be x itself (each row is read whole before it is written), nothing else
+  const int64_t hb = span_bytes(n_rows, h_stride, hidden), xb = span_bytes(n_rows, x_stride, hidden);
+  if (h != x && overlaps(h, hb, x, xb)) return H3ATTN_EINVAL;
+  rc = check_device();
+  if (rc != H3ATTN_OK) return rc;
+  return h3::launch_adaln(a, static_cast<hipStream_t>(stream)) == hipSuccess ? H3ATTN_OK : H3ATTN_EHIP;
+}
+
+extern "C" int h3attn_adaln_residual(const void* x, const void* y, int64_t xy_stride, const int32_t* t_idx,
+                                     const int32_t* tags, const void* gate, const void* shift, const void* scale,
+                                     int64_t entry_stride, int32_t n_entries, void* x_out, void* h,
+                                     int64_t out_stride, int64_t n_rows, int32_t hidden, int32_t norm_kind,
+                                     float eps, void* stream) {
+  h3::AdalnArgs a;
+  std::memset(&a, 0, sizeof(a));
+  int rc = adaln_common(x, xy_stride, t_idx, tags, shift, scale, entry_stride, n_entries, h, out_stride, n_rows,
+                        hidden, norm_kind, eps, &a);
+  if (rc != H3ATTN_OK) return rc;
+  if (y == nullptr || gate == nullptr || x_out == nullptr) return H3ATTN_EINVAL;
+  if (!aligned16(y) || !aligned16(gate) || !aligned16(x_out)) return H3ATTN_EINVAL;
+  if (n_rows == 0) return H3ATTN_OK;
+  // x_out may be x itself; h overlaps nothing; x_out overlaps neither y nor h
+  const int64_t ib = span_bytes(n_rows, xy_stride, hidden), ob = span_bytes(n_rows, out_stride, hidden);
+  if (overlaps(h, ob, x, ib) || overlaps(h, ob, y, ib) || overlaps(h, ob, x_out, ob)) return H3ATTN_EINVAL;
+  if (overlaps(x_out, ob, y, ib)) return H3ATTN_EINVAL;
+  if (x_out != x && overlaps(x_out, ob, x, ib)) return H3ATTN_EINVAL;
+  if (x_out == x && out_stride != xy_stride) return H3ATTN_EINVAL;
+  rc = check_device();
+  if (rc != H3ATTN_OK) return rc;
+  a.y = static_cast<const uint16_t*>(y);
+  a.y_stride = xy_stride;
+  a.gate = static_cast<const uint16_t*>(gate);
+  a.x_out = static_cast<uint16_t*>(x_out);
+  a.out_stride = out_stride;
+  return h3::launch_adaln(a, static_cast<hipStream_t>(stream)) == hipSuccess ? H3ATTN_OK : H3ATTN_EHIP;
+}
+
 extern "C" const char* h3attn_strerror(int code) {
   switch (code) {
     case H3ATTN_OK: return "ok";
@@ -150,4 +237,4 @@ extern "C" const char* h3attn_strerror(int code) {
   }
 }
 
-extern "C" const char* h3attn_version(void) { return "h3attn 0.1.0 gfx950"; }
+extern "C" const char* h3attn_version(void) { return "h3attn 0.2.0 gfx950"; }

@@ -39,7 +39,30 @@ struct FwdArgs {
   RopeTable tab;
 };
 
+struct AdalnArgs {
+  const uint16_t* x;       // bf16 [n_rows][x_stride]
+  const uint16_t* y;       // bf16 [n_rows][y_stride]; null selects the plain modulation
+  const int32_t* t_idx;    // per-row timestep index
+  const int32_t* tags;     // per-row token tag (0 text, 1 video, 2 audio)
+  const uint16_t* gate;    // bf16 table planes: entry e at plane + e * entry_stride
+  const uint16_t* shift;
+  const uint16_t* scale;
+  uint16_t* x_out;         // bf16 residual result (residual form only)
+  uint16_t* h;             // bf16 modulated norm
+  int64_t x_stride;
+  int64_t y_stride;
+  int64_t out_stride;      // rows of x_out
+  int64_t h_stride;
+  int64_t entry_stride;
+  int64_t n_entries;
+  int64_t n_rows;
+  int32_t hidden;
+  int32_t norm_kind;       // 0 layer norm, 1 root-mean-square norm
+  float eps;
+};
+
 hipError_t launch_rope_qk(const RopeArgs& a, hipStream_t stream);
+hipError_t launch_adaln(const AdalnArgs& a, hipStream_t stream);
 hipError_t launch_attn_fwd(const FwdArgs& a, hipStream_t stream);
 
 }  // namespace h3

@@ -161,3 +161,35 @@ def test_abi_rejects_bad_geometry(h3):
 def test_strerror(h3):
     for code in (0, -1, -2, -3, -4, 99):
         assert isinstance(h3.strerror(code), str) and h3.strerror(code)
+
+
+def test_abi_rejects_bad_adaln_calls(h3):
+    lib = h3.load_library()
+    P = 1 << 24
+    X, Y, XO, H, TI, TG, TAB = P, 2 * P, 3 * P, 4 * P, 5 * P, 6 * P, 7 * P
+    C = 5376
+    E, R = h3.H3ATTN_EINVAL, h3.H3ATTN_ERANGE
+
+    def mod(x=X, xs=C, ti=TI, tg=TG, sh=TAB, sc=TAB + 2 * C, es=6 * C, ne=6, h=H, hs=C, n=64, c=C, kind=0,
+            eps=1e-6):
+        return lib.h3attn_adaln_modulate(x, xs, ti, tg, sh, sc, es, ne, h, hs, n, c, kind, eps, None)
+
+    def res(x=X, y=Y, s=C, ti=TI, tg=TG, g=TAB + 4 * C, sh=TAB, sc=TAB + 2 * C, es=6 * C, ne=6, xo=XO, h=H,
+            os_=C, n=64, c=C, kind=0, eps=1e-6):
+        return lib.h3attn_adaln_residual(x, y, s, ti, tg, g, sh, sc, es, ne, xo, h, os_, n, c, kind, eps, None)
+
+    assert mod(n=0) == 0 and res(n=0) == 0                 # empty: no-op
+    assert mod(c=0) == E and mod(c=12) == E and mod(c=8200) == E
+    assert mod(xs=C - 8) == E and mod(hs=C + 4) == E
+    assert mod(kind=2) == E and mod(eps=-1.0) == E and mod(eps=float("nan")) == E
+    assert mod(ne=0) == E and mod(es=-8) == E and mod(es=6 * C + 4) == E
+    assert mod(x=None) == E and mod(ti=None) == E and mod(tg=None) == E and mod(sh=None) == E
+    assert mod(x=X + 8) == E and mod(h=H + 2) == E and mod(ti=TI + 2) == E
+    assert mod(n=-1) == E and mod(n=2 ** 31) == R
+    assert mod(h=X + 1024) == E                            # h overlaps x without being x
+    assert res(y=None) == E and res(g=None) == E and res(xo=None) == E
+    assert res(y=Y + 8) == E and res(xo=XO + 8) == E
+    assert res(h=X) == E and res(h=Y) == E and res(h=XO) == E     # h overlaps an input or x_out
+    assert res(xo=Y) == E                                  # x_out overlaps y
+    assert res(xo=X + 1024) == E                           # x_out overlaps x without being x
+    assert res(xo=X, os_=2 * C) == E                       # in place needs one stride
