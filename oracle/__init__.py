@@ -12,7 +12,8 @@ statement of what the hot path computes, written from the pages:
 * "MiniMax Opens H3 Base Weights ..." (full attention only in the open release),
 * AdaLN: the AdaLN paragraphs of the explainer page (norm(x) * (1 + scale) +
   shift, index = timestep_index * 3 + token_tag) and section 5 of the thread
-  (shift, scale and gate per block for the attention and MLP paths).
+  (shift, scale and gate per block for the attention and MLP paths),
+* packing: the explainer's patchify, latent-frame and flow-matching paragraphs.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import it.  It shares no code with the HIP library and imports
@@ -23,11 +24,13 @@ Modules:
   rope       - three-axis rotary embedding of Q / K, float64
   attention  - softmax(QK^T * scale) V per head, float64, plus log-sum-exp
   adaln      - per-row indexed modulation, the gated residual, float64
+  pack       - 1x2x2 patchify of video latents, audio packing, the Euler step
 """
 from .coords import build_coords, f32_round, video_hw_f64
 from .rope import inv_freq, rope
 from .attention import attention, bf16_bits_to_f64
 from . import adaln
+from . import pack
 
 __all__ = ["build_coords", "f32_round", "video_hw_f64", "inv_freq", "rope",
-           "attention", "bf16_bits_to_f64", "adaln"]
+           "attention", "bf16_bits_to_f64", "adaln", "pack"]

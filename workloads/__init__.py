@@ -141,3 +141,21 @@ def adaln_inputs(n, c=ADALN_HIDDEN, n_timesteps=2, seed=DEFAULT_SEED, table_scal
     y = normal_bf16((n, c), seed + 11)
     table = normal_bf16((n_timesteps * 3, ADALN_PARAMS, c), seed + 12, table_scale)
     return x, y, table
+
+
+# ---- latent packing inputs (sampler state and velocity tokens)
+VIDEO_LATENT_CHANNELS = 24    # channels per latent cell
+AUDIO_LATENT_WIDTH = 32       # values per audio latent frame and channel
+
+
+def latent_inputs(frames, lat_h, lat_w, audio_steps, n_ch=2, seed=DEFAULT_SEED):
+    """Sampler state and velocities of one target clip: video latent float32 [24][frames][lat_h][lat_w],
+    its velocity tokens bf16 bits [frames * lat_h/2 * lat_w/2][96], audio latent float32
+    [n_ch][audio_steps][32] and its velocity tokens bf16 bits [audio_steps * n_ch][32]; seeds +20..+23."""
+    c = VIDEO_LATENT_CHANNELS
+    video = np.random.default_rng(seed + 20).standard_normal((c, frames, lat_h, lat_w), dtype=np.float32)
+    v_video = normal_bf16((frames * (lat_h // 2) * (lat_w // 2), 4 * c), seed + 21)
+    audio = np.random.default_rng(seed + 22).standard_normal((n_ch, audio_steps, AUDIO_LATENT_WIDTH),
+                                                             dtype=np.float32)
+    v_audio = normal_bf16((audio_steps * n_ch, AUDIO_LATENT_WIDTH), seed + 23)
+    return video, v_video, audio, v_audio
