@@ -14,6 +14,12 @@ gated residual of a sublayer fused with the next modulated layer norm) over
 the same 28,192 rows x 5,376 hidden, per-row table entries timestep * 3 + tag;
 bytes counted per step: x, y read, x_out, h written (2 B each per element),
 the int32 selectors and the three table planes once.
+
+--path pack times one sampler step on the 5 s target clip: the Euler update of
+the float32 video latent [24][31][44][80] from its 27,280 bf16 velocity tokens
+fused with re-packing it into 1x2x2 tokens, then the same for the stereo audio
+latent [2][200][32]; bytes counted per value: 4 + 4 (state) + 2 (velocity) +
+2 (token).
 """
 import argparse
 import json
@@ -168,6 +174,85 @@ def bench_adaln(args):
     print(json.dumps(rec), flush=True)
 
 
+PACK_METRIC = "Euler step + 1x2x2 re-pack of the 5 s target latents GB/s & % HBM peak (27,280 video + 400 audio tokens)"
+PACK_SOURCE = os.path.join(CSRC, "pack_kernel.hip")
+
+
+def pack_cpu_baseline(video, v_video, audio, v_audio, dt, budget_s):
+    """Time the fp64 oracle of the same step, repeated up to ~budget_s."""
+    from oracle import pack as Pk
+    from oracle import adaln as A
+    vv, va = A.bf16_bits_to_f64(v_video), A.bf16_bits_to_f64(v_audio)
+    reps, t_used = 0, 0.0
+    while t_used < budget_s and reps < 50:
+        t0 = time.perf_counter()
+        Pk.video_euler_pack(video, vv, dt)
+        Pk.audio_euler_pack(audio, va, dt)
+        t_used += time.perf_counter() - t0
+        reps += 1
+    nbytes = 12 * (video.size + audio.size)
+    return {"value": reps * nbytes / t_used / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "%d full steps of the 5 s clip, %.1f s of fp64 numpy" % (reps, t_used)}
+
+
+def bench_pack(args):
+    import torch
+    import stream_audio_video_amd as h3
+    h3.load_library()
+    dev = torch.device("cuda:0")
+    frames, lh, lw, steps = 31, 44, 80, 200
+    c, aw = W.VIDEO_LATENT_CHANNELS, W.AUDIO_LATENT_WIDTH
+    video, v_video, audio, v_audio = W.latent_inputs(frames, lh, lw, steps)
+    to_dev = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)
+    vl, al = torch.from_numpy(video).to(dev), torch.from_numpy(audio).to(dev)
+    vv, av = to_dev(v_video), to_dev(v_audio)
+    vt = torch.empty((v_video.shape[0], 4 * c), dtype=torch.bfloat16, device=dev)
+    at = torch.empty((v_audio.shape[0], aw), dtype=torch.bfloat16, device=dev)
+    dt = 1.0 / 49
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        h3.video_euler_pack(vl, c, frames, lh, lw, vv, 4 * c, dt, vt, 4 * c)
+        if ev is not None:
+            ev[1].record()
+        h3.audio_euler_pack(al, 2, steps, aw, av, aw, dt, at, aw)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    v_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    a_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    nbytes = 12 * (video.size + audio.size)
+    v_bytes = 12 * video.size
+    cpu = pack_cpu_baseline(video, v_video, audio, v_audio, dt, args.cpu_budget) if args.cpu_budget > 0 else None
+    rec = {
+        "metric": PACK_METRIC, "value": round(nbytes / (ms_step * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "5 s target clip: video latent 24x31x44x80 (27,280 tokens of 96), audio latent "
+                               "2x200x32 (400 tokens of 32), dt = 1/49",
+                   "video_kernel_ms": round(v_ms, 4), "audio_kernel_ms": round(a_ms, 4), "bytes_per_step": nbytes},
+        "roofline": {"bound": "hbm", "achieved": round(v_bytes / (v_ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(v_bytes / (v_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                     "traffic": measured_traffic(os.path.join(ROOT, "profiles", "pack_video_5s_hbm_traffic.json"),
+                                                 PACK_SOURCE, "pack_sha256")},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -175,7 +260,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="5s", choices=list(W.CONFIGS))
     ap.add_argument("--mode", default="fused", choices=["fused", "prerotated"])
-    ap.add_argument("--path", default="attention", choices=["attention", "adaln"],
+    ap.add_argument("--path", default="attention", choices=["attention", "adaln", "pack"],
                     help="attention: MM-RoPE + attention (the headline); adaln: the AdaLN residual row")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing (0 = skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -196,6 +281,9 @@ def main():
         sys.exit(2)
     if args.path == "adaln":
         bench_adaln(args)
+        return
+    if args.path == "pack":
+        bench_pack(args)
         return
 
     import torch

@@ -203,6 +203,45 @@ int h3attn_adaln_residual(const void* x, const void* y, int64_t xy_stride, const
                           int64_t out_stride, int64_t n_rows, int32_t hidden, int32_t norm_kind,
                           float eps, void* stream);
 
+/*
+ * ---- Latent <-> token packing with the sampler's Euler step ----
+ *
+ * Sources: "MiniMax H3 - one transformer that denoises video and audio
+ * together": patchify paragraph (every non-overlapping 1 x 2 x 2 block of the
+ * video latent becomes one token of 24 x 2 x 2 = 96 values), latent-frame
+ * paragraph (44 x 80 sheet -> 22 x 40 = 880 tokens; one audio latent frame = one
+ * 32-value token per stereo channel), flow-matching paragraphs (x_t = t x0 +
+ * (1 - t) noise; a non-learned scheduler steps along the predicted velocity);
+ * "Inside MiniMax H3: One DiT Stream for Text, Video, and Stereo Audio",
+ * section 2 (only target rows are updated).
+ *
+ * Readings where the pages are silent: the sampler state is float32, tokens
+ * bf16 (nearest even); one step is x <- x + dt * v with dt = t_next - t; the
+ * video latent is [C][T][H][W] and its token rows run (t, patch row, patch
+ * column) with values (c, iy, ix) at (c * 2 + iy) * 2 + ix; the audio latent is
+ * [n_ch][steps][width] and token row s * n_ch + ch holds latent[ch][s][:].
+ *
+ * Both calls: latent is device float32 (8-byte aligned), updated in place when
+ * v_tokens is not NULL (latent += dt * unpack(v_tokens)); tokens, when not NULL,
+ * receive the packed (updated) latent as bf16.  At least one of v_tokens and
+ * tokens must be given.  Token buffers are row-major with a stride in elements
+ * (even, >= the token width), 4-byte aligned, and overlap neither each other
+ * nor the latent.  Zero frames / steps is a no-op.  Errors: EINVAL, ERANGE (more
+ * than 2^31 - 1 latent values; video rows wider than LDS allows:
+ * channels * lat_w > 8192), EUNSUPPORTED, EHIP.
+ */
+
+/* Video: latent [channels][frames][lat_h][lat_w] (lat_h, lat_w even); tokens
+ * [frames * lat_h/2 * lat_w/2][4 * channels]. */
+int h3attn_video_euler_pack(float* latent, int32_t channels, int32_t frames, int32_t lat_h, int32_t lat_w,
+                            const void* v_tokens, int64_t v_stride, float dt, void* tokens,
+                            int64_t tokens_stride, void* stream);
+
+/* Audio: latent [n_ch][steps][width] (width even); tokens [steps * n_ch][width]. */
+int h3attn_audio_euler_pack(float* latent, int32_t n_ch, int32_t steps, int32_t width,
+                            const void* v_tokens, int64_t v_stride, float dt, void* tokens,
+                            int64_t tokens_stride, void* stream);
+
 /* Static description of an error code (never NULL). */
 const char* h3attn_strerror(int code);
 

@@ -12,6 +12,9 @@ device memory and the current stream.  The functions keep the C names:
                  n_rows, hidden, norm_kind=LAYER_NORM, eps=1e-6, stream=None)
   adaln_residual(x, y, xy_stride, t_idx, tags, gate, shift, scale, entry_stride, n_entries,
                  x_out, h, out_stride, n_rows, hidden, norm_kind=LAYER_NORM, eps=1e-6, stream=None)
+  video_euler_pack(latent, channels, frames, lat_h, lat_w, v_tokens, v_stride, dt, tokens, tokens_stride,
+                   stream=None)
+  audio_euler_pack(latent, n_ch, steps, width, v_tokens, v_stride, dt, tokens, tokens_stride, stream=None)
   strerror(code), version()
 
 Tensor arguments may be torch tensors (their data_ptr is passed) or raw
@@ -31,7 +34,8 @@ LAYER_NORM, RMS_NORM = 0, 1
 ADALN_MAX_HIDDEN = 8192
 
 EXPORTED = ("h3attn_build_coords", "h3attn_rope_qk", "h3attn_forward", "h3attn_adaln_modulate",
-            "h3attn_adaln_residual", "h3attn_strerror", "h3attn_version")
+            "h3attn_adaln_residual", "h3attn_video_euler_pack", "h3attn_audio_euler_pack", "h3attn_strerror",
+            "h3attn_version")
 
 
 class H3AttnError(RuntimeError):
@@ -77,6 +81,10 @@ def load_library(path=None):
     lib.h3attn_adaln_residual.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp, i64, i32, vp, vp, i64, i64, i32, i32,
                                           ctypes.c_float, vp]
     lib.h3attn_adaln_residual.restype = ctypes.c_int
+    lib.h3attn_video_euler_pack.argtypes = [vp, i32, i32, i32, i32, vp, i64, ctypes.c_float, vp, i64, vp]
+    lib.h3attn_video_euler_pack.restype = ctypes.c_int
+    lib.h3attn_audio_euler_pack.argtypes = [vp, i32, i32, i32, vp, i64, ctypes.c_float, vp, i64, vp]
+    lib.h3attn_audio_euler_pack.restype = ctypes.c_int
     lib.h3attn_strerror.argtypes = [ctypes.c_int]
     lib.h3attn_strerror.restype = ctypes.c_char_p
     lib.h3attn_version.argtypes = []
@@ -172,6 +180,22 @@ def adaln_residual(x, y, xy_stride, t_idx, tags, gate, shift, scale, entry_strid
                                     float(eps), _stream(stream))
     if rc != H3ATTN_OK:
         raise H3AttnError("h3attn_adaln_residual", rc)
+
+
+def video_euler_pack(latent, channels, frames, lat_h, lat_w, v_tokens, v_stride, dt, tokens, tokens_stride,
+                     stream=None):
+    rc = _L().h3attn_video_euler_pack(_ptr(latent), int(channels), int(frames), int(lat_h), int(lat_w),
+                                      _ptr(v_tokens), int(v_stride), float(dt), _ptr(tokens), int(tokens_stride),
+                                      _stream(stream))
+    if rc != H3ATTN_OK:
+        raise H3AttnError("h3attn_video_euler_pack", rc)
+
+
+def audio_euler_pack(latent, n_ch, steps, width, v_tokens, v_stride, dt, tokens, tokens_stride, stream=None):
+    rc = _L().h3attn_audio_euler_pack(_ptr(latent), int(n_ch), int(steps), int(width), _ptr(v_tokens),
+                                      int(v_stride), float(dt), _ptr(tokens), int(tokens_stride), _stream(stream))
+    if rc != H3ATTN_OK:
+        raise H3AttnError("h3attn_audio_euler_pack", rc)
 
 
 def mmrope_attention(q, k, v, coords_dev, cfg=None, scale=0.0, want_lse=True, fuse_q=True, k_rot=None,

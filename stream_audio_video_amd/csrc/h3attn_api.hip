@@ -226,6 +226,81 @@ extern "C" int h3attn_adaln_residual(const void* x, const void* y, int64_t xy_st
   return h3::launch_adaln(a, static_cast<hipStream_t>(stream)) == hipSuccess ? H3ATTN_OK : H3ATTN_EHIP;
 }
 
+namespace {
+
+// Shared checks of the packing calls (sizes already checked by the caller).
+int pack_common(float* latent, int64_t elems, const void* v, int64_t v_stride, void* tokens, int64_t tok_stride,
+                int64_t rows, int64_t width, float dt) {
+  if (latent == nullptr || (reinterpret_cast<uintptr_t>(latent) & 7u) != 0) return H3ATTN_EINVAL;
+  if (v == nullptr && tokens == nullptr) return H3ATTN_EINVAL;
+  if (!std::isfinite(dt)) return H3ATTN_EINVAL;
+  if (elems >= (int64_t(1) << 31)) return H3ATTN_ERANGE;
+  if (v != nullptr && ((reinterpret_cast<uintptr_t>(v) & 3u) != 0 || v_stride < width || (v_stride & 1) != 0))
+    return H3ATTN_EINVAL;
+  if (tokens != nullptr &&
+      ((reinterpret_cast<uintptr_t>(tokens) & 3u) != 0 || tok_stride < width || (tok_stride & 1) != 0))
+    return H3ATTN_EINVAL;
+  if (rows == 0) return H3ATTN_OK;
+  const int64_t lat_bytes = elems * 4;
+  if (v != nullptr && overlaps(v, span_bytes(rows, v_stride, width), latent, lat_bytes)) return H3ATTN_EINVAL;
+  if (tokens != nullptr) {
+    const int64_t tb = span_bytes(rows, tok_stride, width);
+    if (overlaps(tokens, tb, latent, lat_bytes)) return H3ATTN_EINVAL;
+    if (v != nullptr && overlaps(tokens, tb, v, span_bytes(rows, v_stride, width))) return H3ATTN_EINVAL;
+  }
+  return check_device();
+}
+
+}  // namespace
+
+extern "C" int h3attn_video_euler_pack(float* latent, int32_t channels, int32_t frames, int32_t lat_h, int32_t lat_w,
+                                       const void* v_tokens, int64_t v_stride, float dt, void* tokens,
+                                       int64_t tokens_stride, void* stream) {
+  if (channels < 1 || frames < 0 || lat_h < 2 || lat_w < 2 || (lat_h & 1) != 0 || (lat_w & 1) != 0)
+    return H3ATTN_EINVAL;
+  if (int64_t(channels) * 2 * lat_w * 4 > 65536) return H3ATTN_ERANGE;   // two latent rows of every channel in LDS
+  const int64_t elems = int64_t(channels) * frames * lat_h * lat_w;
+  const int64_t rows = int64_t(frames) * (lat_h / 2) * (lat_w / 2);
+  int rc = pack_common(latent, elems, v_tokens, v_stride, tokens, tokens_stride, rows, 4 * int64_t(channels), dt);
+  if (rc != H3ATTN_OK || rows == 0) return rc;
+  h3::PackArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.latent = latent;
+  a.v = static_cast<const uint16_t*>(v_tokens);
+  a.tokens = static_cast<uint16_t*>(tokens);
+  a.v_stride = v_stride;
+  a.tok_stride = tokens_stride;
+  a.c = channels;
+  a.t = frames;
+  a.h = lat_h;
+  a.w = lat_w;
+  a.dt = dt;
+  return h3::launch_video_pack(a, static_cast<hipStream_t>(stream)) == hipSuccess ? H3ATTN_OK : H3ATTN_EHIP;
+}
+
+extern "C" int h3attn_audio_euler_pack(float* latent, int32_t n_ch, int32_t steps, int32_t width,
+                                       const void* v_tokens, int64_t v_stride, float dt, void* tokens,
+                                       int64_t tokens_stride, void* stream) {
+  if (n_ch < 1 || steps < 0 || width < 2 || (width & 1) != 0) return H3ATTN_EINVAL;
+  const int64_t elems = int64_t(n_ch) * steps * width;
+  const int64_t rows = int64_t(n_ch) * steps;
+  int rc = pack_common(latent, elems, v_tokens, v_stride, tokens, tokens_stride, rows, width, dt);
+  if (rc != H3ATTN_OK || rows == 0) return rc;
+  h3::PackArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.latent = latent;
+  a.v = static_cast<const uint16_t*>(v_tokens);
+  a.tokens = static_cast<uint16_t*>(tokens);
+  a.v_stride = v_stride;
+  a.tok_stride = tokens_stride;
+  a.c = n_ch;
+  a.t = steps;
+  a.h = 1;
+  a.w = width;
+  a.dt = dt;
+  return h3::launch_audio_pack(a, static_cast<hipStream_t>(stream)) == hipSuccess ? H3ATTN_OK : H3ATTN_EHIP;
+}
+
 extern "C" const char* h3attn_strerror(int code) {
   switch (code) {
     case H3ATTN_OK: return "ok";

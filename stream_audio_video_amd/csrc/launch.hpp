@@ -61,7 +61,22 @@ struct AdalnArgs {
   float eps;
 };
 
+struct PackArgs {
+  float* latent;           // float32 sampler state (updated in place when v is set)
+  const uint16_t* v;       // bf16 velocity tokens, or null (no update)
+  uint16_t* tokens;        // bf16 tokens out, or null
+  int64_t v_stride;        // elements between token rows
+  int64_t tok_stride;
+  int32_t c;               // video: channels      | audio: stereo channels
+  int32_t t;               // video: latent frames | audio: steps
+  int32_t h;               // video: latent rows   | audio: 1
+  int32_t w;               // video: latent cols   | audio: values per frame
+  float dt;
+};
+
 hipError_t launch_rope_qk(const RopeArgs& a, hipStream_t stream);
+hipError_t launch_video_pack(const PackArgs& a, hipStream_t stream);
+hipError_t launch_audio_pack(const PackArgs& a, hipStream_t stream);
 hipError_t launch_adaln(const AdalnArgs& a, hipStream_t stream);
 hipError_t launch_attn_fwd(const FwdArgs& a, hipStream_t stream);
 

@@ -1,0 +1,112 @@
+// Latent <-> token packing with the sampler's Euler step, for gfx950.
+//
+// "MiniMax H3 - one transformer that denoises video and audio together":
+// patchify takes every non-overlapping 1 x 2 x 2 block of the video latent and
+// glues its 24 x 2 x 2 channel values into one 96-value token (44 x 80 latent
+// sheet -> 22 x 40 = 880 tokens per latent frame); one audio latent frame is one
+// 32-value token per stereo channel; generation runs a non-learned scheduler
+// step along the predicted velocity, x <- x + dt * v, and only the target rows
+// move ("Inside MiniMax H3: One DiT Stream for Text, Video, and Stereo Audio",
+// section 2).
+//
+// Layouts: video latent float32 [C][T][H][W]; token row (t, py, px) =
+// (t * H/2 + py) * W/2 + px, value (c, iy, ix) at (c * 2 + iy) * 2 + ix.  Audio
+// latent float32 [n_ch][steps][width]; token row s * n_ch + ch = latent[ch][s].
+// The state stays float32 (one fused multiply-add per element); tokens are
+// bfloat16, nearest even.
+//
+// Video: one workgroup per (latent frame, patch row).  The two latent rows of
+// every channel are read coalesced into LDS, updated and emitted in token order
+// (velocity reads and token writes are contiguous rows), then written back
+// coalesced.  HBM-bound: 4 + 4 B of state and 2 + 2 B of tokens per element.
+#include "launch.hpp"
+
+namespace h3 {
+namespace {
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kPackThreads = 256;
+
+__device__ __forceinline__ f32x2_t bf16x2_to_f32(uint32_t w) {
+  return f32x2_t{__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u)};
+}
+
+__global__ __launch_bounds__(kPackThreads) void video_pack_kernel(PackArgs a) {
+  extern __shared__ float tile[];   // [C][2][W]
+  const int hp = a.h >> 1, wp = a.w >> 1;
+  const int t = blockIdx.x / hp, py = blockIdx.x - t * hp;
+  const int two_w = 2 * a.w;
+  const int n = a.c * two_w;        // elements of the two latent rows, all channels
+  const int64_t plane = int64_t(a.t) * a.h * a.w;
+  float* lat = a.latent + (int64_t(t) * a.h + 2 * py) * a.w;   // channel 0, row 2 py
+
+  // latent rows -> LDS (pairs along x)
+  for (int e = 2 * threadIdx.x; e < n; e += 2 * kPackThreads) {
+    const int c = e / two_w, rem = e - c * two_w;   // rem = iy * W + x, x even
+    *reinterpret_cast<f32x2_t*>(tile + e) = *reinterpret_cast<const f32x2_t*>(lat + c * plane + rem);
+  }
+  __syncthreads();
+
+  // token order: pair p of token px covers values 2 jp, 2 jp + 1 = (c, iy, ix = 0 / 1)
+  const int64_t row0 = int64_t(blockIdx.x) * wp;
+  const int pairs_per_token = 2 * a.c;
+  for (int p = threadIdx.x; p < a.c * a.w; p += kPackThreads) {
+    const int px = p / pairs_per_token, jp = p - px * pairs_per_token;
+    const int c = jp >> 1, iy = jp & 1;
+    float* cell = tile + c * two_w + iy * a.w + 2 * px;
+    f32x2_t v = *reinterpret_cast<f32x2_t*>(cell);
+    if (a.v != nullptr) {
+      const f32x2_t d = bf16x2_to_f32(*reinterpret_cast<const uint32_t*>(a.v + (row0 + px) * a.v_stride + 2 * jp));
+      v = f32x2_t{__builtin_fmaf(a.dt, d[0], v[0]), __builtin_fmaf(a.dt, d[1], v[1])};
+      *reinterpret_cast<f32x2_t*>(cell) = v;
+    }
+    if (a.tokens != nullptr)
+      *reinterpret_cast<uint32_t*>(a.tokens + (row0 + px) * a.tok_stride + 2 * jp) = pack_bf16x2(v[0], v[1]);
+  }
+
+  if (a.v == nullptr) return;
+  __syncthreads();
+  for (int e = 2 * threadIdx.x; e < n; e += 2 * kPackThreads) {
+    const int c = e / two_w, rem = e - c * two_w;
+    *reinterpret_cast<f32x2_t*>(lat + c * plane + rem) = *reinterpret_cast<const f32x2_t*>(tile + e);
+  }
+}
+
+// audio: a = (n_ch, steps, width) in (c, t, w); one thread per value pair
+__global__ __launch_bounds__(kPackThreads) void audio_pack_kernel(PackArgs a) {
+  const int half = a.w >> 1;
+  const int64_t total = int64_t(a.t) * a.c * half;
+  const int64_t p = int64_t(blockIdx.x) * kPackThreads + threadIdx.x;
+  if (p >= total) return;
+  const int64_t row = p / half;                      // token row s * n_ch + ch
+  const int j = 2 * int(p - row * half);
+  const int64_t s = row / a.c, ch = row - s * a.c;
+  float* cell = a.latent + (ch * a.t + s) * a.w + j;
+  f32x2_t v = *reinterpret_cast<f32x2_t*>(cell);
+  if (a.v != nullptr) {
+    const f32x2_t d = bf16x2_to_f32(*reinterpret_cast<const uint32_t*>(a.v + row * a.v_stride + j));
+    v = f32x2_t{__builtin_fmaf(a.dt, d[0], v[0]), __builtin_fmaf(a.dt, d[1], v[1])};
+    *reinterpret_cast<f32x2_t*>(cell) = v;
+  }
+  if (a.tokens != nullptr) *reinterpret_cast<uint32_t*>(a.tokens + row * a.tok_stride + j) = pack_bf16x2(v[0], v[1]);
+}
+
+}  // namespace
+
+hipError_t launch_video_pack(const PackArgs& a, hipStream_t stream) {
+  void* args[] = {const_cast<PackArgs*>(&a)};
+  const size_t lds = size_t(a.c) * 2 * a.w * sizeof(float);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&video_pack_kernel), dim3(a.t * (a.h >> 1)),
+                         dim3(kPackThreads), args, lds, stream);
+}
+
+hipError_t launch_audio_pack(const PackArgs& a, hipStream_t stream) {
+  void* args[] = {const_cast<PackArgs*>(&a)};
+  const int64_t total = int64_t(a.t) * a.c * (a.w >> 1);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&audio_pack_kernel),
+                         dim3(static_cast<unsigned>((total + kPackThreads - 1) / kPackThreads)), dim3(kPackThreads),
+                         args, 0, stream);
+}
+
+}  // namespace h3

@@ -193,3 +193,27 @@ def test_abi_rejects_bad_adaln_calls(h3):
     assert res(xo=Y) == E                                  # x_out overlaps y
     assert res(xo=X + 1024) == E                           # x_out overlaps x without being x
     assert res(xo=X, os_=2 * C) == E                       # in place needs one stride
+
+
+def test_abi_rejects_bad_pack_calls(h3):
+    lib = h3.load_library()
+    P = 1 << 24
+    L, V, T = P, 4 * P, 8 * P
+    E, R = h3.H3ATTN_EINVAL, h3.H3ATTN_ERANGE
+
+    def vid(lat=L, c=24, f=31, h=44, w=80, v=V, vs=96, dt=0.1, t=T, ts=96):
+        return lib.h3attn_video_euler_pack(lat, c, f, h, w, v, vs, dt, t, ts, None)
+
+    def aud(lat=L, ch=2, s=200, w=32, v=V, vs=32, dt=0.1, t=T, ts=32):
+        return lib.h3attn_audio_euler_pack(lat, ch, s, w, v, vs, dt, t, ts, None)
+
+    assert vid(f=0) == 0 and aud(s=0) == 0                  # empty: no-op
+    assert vid(v=None, t=None) == E and aud(v=None, t=None) == E
+    assert vid(lat=None) == E and vid(lat=L + 4) == E and vid(v=V + 2) == E and vid(t=T + 2) == E
+    assert vid(c=0) == E and vid(f=-1) == E and vid(h=43) == E and vid(w=81) == E and vid(h=0) == E
+    assert vid(vs=94) == E and vid(ts=97) == E and vid(dt=float("inf")) == E
+    assert vid(c=24, w=344) == R                             # two latent rows of every channel exceed LDS
+    assert vid(c=4, f=2 ** 20, h=32, w=32) == R              # more than 2^31 latent values
+    assert vid(t=L + 4096) == E and vid(v=L) == E and vid(t=V + 64) == E   # overlaps
+    assert aud(ch=0) == E and aud(s=-1) == E and aud(w=31) == E and aud(w=0) == E
+    assert aud(vs=30) == E and aud(ts=33) == E and aud(v=L) == E and aud(t=L) == E
