@@ -1,0 +1,109 @@
+"""Reference-row K/V reuse across sampler steps, through the C ABI (MI355X, gfx950).
+
+"MiniMax H3 - one transformer that denoises video and audio together",
+cross-step-cache paragraph: the transformer runs from scratch every step; text
+rows inherit the moving video timestep, and after the first block the changing
+target rows flow into every row.  So only the first block's reference rows
+(clean context, fixed timestep) see the same K and V at every step.  Reuse =
+keep their rotated K and their V in the persistent buffers the attention reads,
+and at each step rotate only the fresh rows (text and targets) into place
+(h3attn_rope_qk on row sub-ranges: pointer offsets, no copy of the cache).
+The result must equal a full recompute bit for bit, and the oracle to the
+attention tolerances.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+SEC, TH = W.ROPE_SECTIONS, W.ROPE_THETAS
+
+
+def dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def host_bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+# text, two reference stills, one reference audio clip, then the target clip
+SEGS = [W.text(40, -80), W.video(1, 4, 8, t0_thirds=-60), W.video(1, 4, 8, t0_thirds=-40), W.audio(16, -40),
+        W.video(2, 4, 8), W.audio(20, 0)]
+HEADS = 3
+
+
+def fresh_ranges(segs):
+    """Row ranges that change every step: text and target media (references start before t = 0)."""
+    out, r = [], 0
+    for s in segs:
+        n = s.frames * s.grid_h * s.grid_w
+        if s.kind == W.TEXT or s.t0_thirds >= 0:
+            if out and out[-1][1] == r:
+                out[-1] = (out[-1][0], r + n)
+            else:
+                out.append((r, r + n))
+        r += n
+    return out
+
+
+@pytest.mark.parametrize("segs,heads", [(SEGS, HEADS), (W.CONFIGS["ref2va"][1], 42)])
+def test_reference_kv_reuse_equals_full_recompute(gpu_lib, segs, heads):
+    h3 = gpu_lib
+    n = W.n_tokens(segs)
+    cfg = h3.rope_cfg()
+    coords = torch.from_numpy(h3.build_coords(segs)).cuda()
+    q1, k1, v1 = W.qkv(n, heads, seed=11)
+    q2, k2, v2 = W.qkv(n, heads, seed=111)        # disjoint from seeds 11..13 of step 1
+    ranges = fresh_ranges(segs)
+    ref_rows = np.ones(n, bool)
+    for a, b in ranges:
+        ref_rows[a:b] = False
+    assert ref_rows.any() and not ref_rows.all()
+    # step 2 keeps the reference rows' K and V of step 1
+    k2[ref_rows], v2[ref_rows] = k1[ref_rows], v1[ref_rows]
+    stride = heads * 128
+
+    # step 1: rotate every K into the persistent buffer
+    kt = torch.empty((n, heads, 128), dtype=torch.bfloat16, device="cuda")
+    vp = dev_bf16(v1)
+    h3.rope_qk(cfg, coords, None, None, dev_bf16(k1), kt, n, heads, stride)
+    o = torch.empty_like(kt)
+    lse = torch.empty((heads, n), dtype=torch.float32, device="cuda")
+    h3.forward(cfg, coords, 1, dev_bf16(q1), kt, vp, o, lse, n, heads, stride, stride)
+
+    # step 2: only the fresh rows are rotated into place; reference rows stay cached
+    kf, vf, qf = dev_bf16(k2), dev_bf16(v2), dev_bf16(q2)
+    esz = 2
+    for a, b in ranges:
+        h3.rope_qk(cfg, coords.data_ptr() + 3 * 4 * a, None, None, kf.data_ptr() + a * stride * esz,
+                   kt.data_ptr() + a * stride * esz, b - a, heads, stride)
+        vp[a:b] = vf[a:b]
+    h3.forward(cfg, coords, 1, qf, kt, vp, o, lse, n, heads, stride, stride)
+
+    # full recompute of step 2
+    kt_full = torch.empty_like(kt)
+    h3.rope_qk(cfg, coords, None, None, kf, kt_full, n, heads, stride)
+    o_full = torch.empty_like(kt)
+    lse_full = torch.empty_like(lse)
+    h3.forward(cfg, coords, 1, qf, kt_full, vf, o_full, lse_full, n, heads, stride, stride)
+    torch.cuda.synchronize()
+    assert torch.equal(kt.view(torch.int16), kt_full.view(torch.int16))
+    assert torch.equal(o.view(torch.int16), o_full.view(torch.int16))
+    assert torch.equal(lse, lse_full)
+
+    # and the oracle (sampled query rows at full size)
+    c = oracle.build_coords(segs)
+    rows = np.arange(n) if n <= 512 else np.sort(np.random.default_rng(3).choice(n, 48, replace=False))
+    hs = list(range(heads)) if heads <= 3 else [0, 41]
+    f64 = oracle.bf16_bits_to_f64
+    o_ref, lse_ref = oracle.attention(f64(q2[:, hs]), f64(k2[:, hs]), f64(v2[:, hs]), c, SEC, TH, rows=rows)
+    got = f64(host_bits(o)[rows][:, hs])
+    err = got - o_ref
+    print("reuse n=%d: max|err| %.3e rms %.3e" % (n, np.max(np.abs(err)), np.sqrt(np.mean(err ** 2))), flush=True)
+    assert np.max(np.abs(err)) <= 2e-2 and np.sqrt(np.mean(err ** 2)) <= 2e-3
+    assert np.max(np.abs(lse.cpu().numpy()[hs][:, rows] - lse_ref)) <= 1e-2
