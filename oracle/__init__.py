@@ -25,12 +25,14 @@ Modules:
   attention  - softmax(QK^T * scale) V per head, float64, plus log-sum-exp
   adaln      - per-row indexed modulation, the gated residual, float64
   pack       - 1x2x2 patchify of video latents, audio packing, the Euler step
+  linear     - the attention projections, with Q and K rotated (fused QKV)
 """
 from .coords import build_coords, f32_round, video_hw_f64
 from .rope import inv_freq, rope
 from .attention import attention, bf16_bits_to_f64
 from . import adaln
 from . import pack
+from . import linear
 
 __all__ = ["build_coords", "f32_round", "video_hw_f64", "inv_freq", "rope",
-           "attention", "bf16_bits_to_f64", "adaln", "pack"]
+           "attention", "bf16_bits_to_f64", "adaln", "pack", "linear"]

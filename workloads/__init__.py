@@ -159,3 +159,13 @@ def latent_inputs(frames, lat_h, lat_w, audio_steps, n_ch=2, seed=DEFAULT_SEED):
                                                              dtype=np.float32)
     v_audio = normal_bf16((audio_steps * n_ch, AUDIO_LATENT_WIDTH), seed + 23)
     return video, v_video, audio, v_audio
+
+
+# ---- projection inputs
+def projection_inputs(m, k, n, seed=DEFAULT_SEED, with_bias=True):
+    """Activations x ~ N(0, 1) bf16 bits [m, k], weight ~ N(0, 1/k) bf16 bits [n, k] (so outputs are
+    ~ unit variance), bias ~ N(0, 0.1^2) bf16 bits [n] or None; seeds +30, +31, +32."""
+    x = normal_bf16((m, k), seed + 30)
+    w = normal_bf16((n, k), seed + 31, 1.0 / np.sqrt(k))
+    b = normal_bf16((n,), seed + 32, 0.1) if with_bias else None
+    return x, w, b
