@@ -20,6 +20,11 @@ the float32 video latent [24][31][44][80] from its 27,280 bf16 velocity tokens
 fused with re-packing it into 1x2x2 tokens, then the same for the stereo audio
 latent [2][200][32]; bytes counted per value: 4 + 4 (state) + 2 (velocity) +
 2 (token).
+
+--path qkv times the fused QKV projection of the 5 s rows with the rotary
+embedding of Q and K in its epilogue (28,192 x 5,376 -> 3 x 42 x 128, bias,
+synthetic weights), FLOP 2 M N K; the output projection (5,376 -> 5,376, no
+rotation) is timed beside it.
 """
 import argparse
 import json
@@ -253,6 +258,92 @@ def bench_pack(args):
     print(json.dumps(rec), flush=True)
 
 
+QKV_METRIC = "Fused QKV projection + Q/K RoPE epilogue TFLOP/s & % bf16 MFMA peak, 28,192 x 5,376 -> 16,128"
+
+
+def qkv_cpu_baseline(x, w, b, coords, budget_s):
+    """Time the fp64 oracle of the fused projection on blocks of 64 rows, ~budget_s."""
+    from oracle.linear import qkv_rope
+    from oracle import bf16_bits_to_f64 as f64
+    wf, bf = f64(w), f64(b)
+    rows_done, t_used = 0, 0.0
+    while t_used < budget_s and rows_done < x.shape[0]:
+        r = slice(rows_done, min(x.shape[0], rows_done + 64))
+        xb = f64(x[r])
+        t0 = time.perf_counter()
+        qkv_rope(xb, wf, bf, coords[r], 42, W.ROPE_SECTIONS, W.ROPE_THETAS)
+        t_used += time.perf_counter() - t0
+        rows_done = r.stop
+    flop = 2.0 * rows_done * w.shape[0] * w.shape[1]
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = 1
+    return {"value": flop / t_used / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": "rows 0..%d of %d (blocks of 64), %.1f s of fp64 numpy; FLOP 2*rows*N*K"
+                      % (rows_done - 1, x.shape[0], t_used)}
+
+
+def bench_qkv(args):
+    import torch
+    import stream_audio_video_amd as h3
+    h3.load_library()
+    dev = torch.device("cuda:0")
+    h, segs = W.CONFIGS[args.config]
+    m, k = W.n_tokens(segs), W.ADALN_HIDDEN
+    n = 3 * h * W.HEAD_DIM
+    x, w, b = W.projection_inputs(m, k, n)
+    _, wo, _ = W.projection_inputs(1, k, k, seed=W.DEFAULT_SEED + 1, with_bias=False)
+    to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    xd, wd, bd, wod = to_dev(x), to_dev(w), to_dev(b), to_dev(wo)
+    coords_h = h3.build_coords(segs)
+    coords = torch.from_numpy(coords_h).to(dev)
+    yd = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    od = torch.empty((m, k), dtype=torch.bfloat16, device=dev)
+    cfg = h3.rope_cfg(W.ROPE_SECTIONS, W.ROPE_THETAS)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        h3.linear(xd, k, wd, k, bd, yd, n, m, n, k, cfg, coords, 2 * h * W.HEAD_DIM)
+        if ev is not None:
+            ev[1].record()
+        h3.linear(xd, k, wod, k, None, od, k, m, k, k)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    qkv_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    out_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    flop_qkv, flop_out = 2.0 * m * n * k, 2.0 * m * k * k
+    achieved = flop_qkv / (qkv_ms * 1e-3) / 1e12
+    cpu = qkv_cpu_baseline(x, w, b, coords_h, args.cpu_budget) if args.cpu_budget > 0 else None
+    rec = {
+        "metric": QKV_METRIC, "value": round((flop_qkv + flop_out) / (ms_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "%s rows %d, hidden %d, fused QKV %d outputs with bias and Q/K rotation; output "
+                               "projection %d -> %d" % (args.config, m, k, n, k, k),
+                   "qkv_ms": round(qkv_ms, 4), "qkv_TFLOPs": round(achieved, 2), "out_proj_ms": round(out_ms, 4),
+                   "out_proj_TFLOPs": round(flop_out / (out_ms * 1e-3) / 1e12, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -262,7 +353,7 @@ def main():
     ap.add_argument("--mode", default="fused", choices=["fused", "prerotated"])
     ap.add_argument("--reuse-refs", action="store_true",
                     help="keep the reference rows' rotated K cached across steps; rotate only text and target rows")
-    ap.add_argument("--path", default="attention", choices=["attention", "adaln", "pack"],
+    ap.add_argument("--path", default="attention", choices=["attention", "adaln", "pack", "qkv"],
                     help="attention: MM-RoPE + attention (the headline); adaln: the AdaLN residual row")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing (0 = skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -286,6 +377,9 @@ def main():
         return
     if args.path == "pack":
         bench_pack(args)
+        return
+    if args.path == "qkv":
+        bench_qkv(args)
         return
 
     import torch

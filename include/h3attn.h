@@ -204,6 +204,37 @@ int h3attn_adaln_residual(const void* x, const void* y, int64_t xy_stride, const
                           float eps, void* stream);
 
 /*
+ * ---- Attention projections with the rotary embedding in the epilogue ----
+ *
+ * Sources: "Inside MiniMax H3: One DiT Stream for Text, Video, and Stereo
+ * Audio", section 2 (every row shares one set of attention projections); "MiniMax
+ * H3 - one transformer that denoises video and audio together", position-chain
+ * paragraph (rope() rotates Q and K, V is not rotated).
+ *
+ * Device call.  y = x W^T (+ bias), then, for the leading rope_cols output
+ * features (whole 128-wide heads), the rotation of h3attn_rope_qk applied to the
+ * float32 results by each row's coordinates, then one rounding to bf16 (nearest
+ * even).  For the fused QKV projection of H heads: W is [3 H 128][k] (Q rows,
+ * then K, then V), rope_cols = 2 H 128, and y = [m][3][H][128] feeds
+ * h3attn_forward with rope_q = 0 through strided views (row stride 3 H 128).
+ * Readings: no bias unless given; W is stored [n_out][k] (row = output feature).
+ *   x          bf16 [m][x_stride], w bf16 [n_out][w_stride], bias bf16 [n_out] or NULL
+ *   y          out: bf16 [m][y_stride]; must not overlap x, w or bias
+ *   n_out      multiple of H3ATTN_LINEAR_TILE (256);  k multiple of H3ATTN_LINEAR_KSTEP (64)
+ *   rope_cfg, coords_dev   as for h3attn_rope_qk; used only when rope_cols > 0
+ *   rope_cols  0 <= rope_cols <= n_out, multiple of 128
+ * Strides are in elements, multiples of 8 (x, w >= k; y >= n_out); pointers
+ * 16-byte aligned.  Arithmetic: float32 accumulation of exact bf16 products.
+ * m == 0 is a no-op.  Errors: EINVAL, ERANGE (m >= 2^31, 256 rows of x or w
+ * spanning 2^31 bytes, x spanning 2^32 bytes), EUNSUPPORTED, EHIP.
+ */
+#define H3ATTN_LINEAR_TILE 256
+#define H3ATTN_LINEAR_KSTEP 64
+int h3attn_linear(const void* x, int64_t x_stride, const void* w, int64_t w_stride, const void* bias,
+                  void* y, int64_t y_stride, int64_t m, int32_t n_out, int32_t k,
+                  const h3attn_rope_cfg* rope_cfg, const float* coords_dev, int32_t rope_cols, void* stream);
+
+/*
  * ---- Latent <-> token packing with the sampler's Euler step ----
  *
  * Sources: "MiniMax H3 - one transformer that denoises video and audio

@@ -15,6 +15,8 @@ device memory and the current stream.  The functions keep the C names:
   video_euler_pack(latent, channels, frames, lat_h, lat_w, v_tokens, v_stride, dt, tokens, tokens_stride,
                    stream=None)
   audio_euler_pack(latent, n_ch, steps, width, v_tokens, v_stride, dt, tokens, tokens_stride, stream=None)
+  linear(x, x_stride, w, w_stride, bias, y, y_stride, m, n_out, k, rope_cfg=None, coords_dev=None,
+         rope_cols=0, stream=None)
   strerror(code), version()
 
 Tensor arguments may be torch tensors (their data_ptr is passed) or raw
@@ -35,7 +37,7 @@ ADALN_MAX_HIDDEN = 8192
 
 EXPORTED = ("h3attn_build_coords", "h3attn_rope_qk", "h3attn_forward", "h3attn_adaln_modulate",
             "h3attn_adaln_residual", "h3attn_video_euler_pack", "h3attn_audio_euler_pack", "h3attn_strerror",
-            "h3attn_version")
+            "h3attn_linear", "h3attn_version")
 
 
 class H3AttnError(RuntimeError):
@@ -85,6 +87,9 @@ def load_library(path=None):
     lib.h3attn_video_euler_pack.restype = ctypes.c_int
     lib.h3attn_audio_euler_pack.argtypes = [vp, i32, i32, i32, vp, i64, ctypes.c_float, vp, i64, vp]
     lib.h3attn_audio_euler_pack.restype = ctypes.c_int
+    lib.h3attn_linear.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, i32, i32, ctypes.POINTER(RopeCfg), vp, i32,
+                                  vp]
+    lib.h3attn_linear.restype = ctypes.c_int
     lib.h3attn_strerror.argtypes = [ctypes.c_int]
     lib.h3attn_strerror.restype = ctypes.c_char_p
     lib.h3attn_version.argtypes = []
@@ -196,6 +201,15 @@ def audio_euler_pack(latent, n_ch, steps, width, v_tokens, v_stride, dt, tokens,
                                       int(v_stride), float(dt), _ptr(tokens), int(tokens_stride), _stream(stream))
     if rc != H3ATTN_OK:
         raise H3AttnError("h3attn_audio_euler_pack", rc)
+
+
+def linear(x, x_stride, w, w_stride, bias, y, y_stride, m, n_out, k, rope_cfg=None, coords_dev=None, rope_cols=0,
+           stream=None):
+    rc = _L().h3attn_linear(_ptr(x), int(x_stride), _ptr(w), int(w_stride), _ptr(bias), _ptr(y), int(y_stride),
+                            int(m), int(n_out), int(k), ctypes.byref(rope_cfg) if rope_cfg is not None else None,
+                            _ptr(coords_dev), int(rope_cols), _stream(stream))
+    if rc != H3ATTN_OK:
+        raise H3AttnError("h3attn_linear", rc)
 
 
 def mmrope_attention(q, k, v, coords_dev, cfg=None, scale=0.0, want_lse=True, fuse_q=True, k_rot=None,

@@ -20,7 +20,8 @@ ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["h3attn_api.hip", "rope_kernel.hip", "attn_fwd.hip", "adaln_kernel.hip", "pack_kernel.hip"]
+HIP_SOURCES = ["h3attn_api.hip", "rope_kernel.hip", "attn_fwd.hip", "adaln_kernel.hip", "pack_kernel.hip",
+               "gemm_kernel.hip"]
 HOST_SOURCES = ["coords.cpp"]
 
 HIP_FLAGS = [

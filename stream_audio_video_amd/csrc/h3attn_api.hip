@@ -301,6 +301,53 @@ extern "C" int h3attn_audio_euler_pack(float* latent, int32_t n_ch, int32_t step
   return h3::launch_audio_pack(a, static_cast<hipStream_t>(stream)) == hipSuccess ? H3ATTN_OK : H3ATTN_EHIP;
 }
 
+extern "C" int h3attn_linear(const void* x, int64_t x_stride, const void* w, int64_t w_stride, const void* bias,
+                             void* y, int64_t y_stride, int64_t m, int32_t n_out, int32_t k,
+                             const h3attn_rope_cfg* rope_cfg, const float* coords_dev, int32_t rope_cols,
+                             void* stream) {
+  h3::GemmArgs a;
+  std::memset(&a, 0, sizeof(a));
+  if (x == nullptr || w == nullptr || y == nullptr) return H3ATTN_EINVAL;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (bias != nullptr && !aligned16(bias))) return H3ATTN_EINVAL;
+  if (m < 0 || n_out <= 0 || (n_out % H3ATTN_LINEAR_TILE) != 0 || k <= 0 || (k % H3ATTN_LINEAR_KSTEP) != 0)
+    return H3ATTN_EINVAL;
+  if (x_stride < k || (x_stride & 7) != 0 || w_stride < k || (w_stride & 7) != 0 || y_stride < n_out ||
+      (y_stride & 7) != 0)
+    return H3ATTN_EINVAL;
+  if (rope_cols < 0 || rope_cols > n_out || (rope_cols % h3::kHeadDim) != 0) return H3ATTN_EINVAL;
+  if (rope_cols > 0) {
+    int rc = make_table(rope_cfg, &a.tab);
+    if (rc != H3ATTN_OK) return rc;
+    if (coords_dev == nullptr) return H3ATTN_EINVAL;
+  }
+  // byte offsets inside a 256-row tile and over x are 32-bit
+  if (m >= (int64_t(1) << 31) || int64_t(H3ATTN_LINEAR_TILE) * x_stride * 2 >= (int64_t(1) << 31) ||
+      int64_t(H3ATTN_LINEAR_TILE) * w_stride * 2 >= (int64_t(1) << 31) || m * x_stride * 2 >= (int64_t(1) << 32))
+    return H3ATTN_ERANGE;
+  if (m == 0) return H3ATTN_OK;
+  const int64_t yb = span_bytes(m, y_stride, n_out);
+  if (overlaps(y, yb, x, span_bytes(m, x_stride, k)) || overlaps(y, yb, w, span_bytes(n_out, w_stride, k)) ||
+      (bias != nullptr && overlaps(y, yb, bias, int64_t(n_out) * 2)))
+    return H3ATTN_EINVAL;
+  int rc = check_device();
+  if (rc != H3ATTN_OK) return rc;
+  a.x = static_cast<const uint16_t*>(x);
+  a.w = static_cast<const uint16_t*>(w);
+  a.bias = static_cast<const uint16_t*>(bias);
+  a.y = static_cast<uint16_t*>(y);
+  a.coords = coords_dev;
+  a.x_stride = x_stride;
+  a.w_stride = w_stride;
+  a.y_stride = y_stride;
+  a.m = static_cast<int32_t>(m);
+  a.n_out = n_out;
+  a.k = k;
+  a.rope_cols = rope_cols;
+  a.tiles_f = n_out / H3ATTN_LINEAR_TILE;
+  a.tiles_t = static_cast<int32_t>((m + H3ATTN_LINEAR_TILE - 1) / H3ATTN_LINEAR_TILE);
+  return h3::launch_gemm(a, static_cast<hipStream_t>(stream)) == hipSuccess ? H3ATTN_OK : H3ATTN_EHIP;
+}
+
 extern "C" const char* h3attn_strerror(int code) {
   switch (code) {
     case H3ATTN_OK: return "ok";

@@ -74,7 +74,26 @@ struct PackArgs {
   float dt;
 };
 
+struct GemmArgs {
+  const uint16_t* x;       // bf16 [m][x_stride]
+  const uint16_t* w;       // bf16 [n_out][w_stride]
+  const uint16_t* bias;    // bf16 [n_out] or null
+  uint16_t* y;             // bf16 [m][y_stride]
+  const float* coords;     // [m][3] when rope_cols > 0
+  int64_t x_stride;
+  int64_t w_stride;
+  int64_t y_stride;
+  int32_t m;
+  int32_t n_out;
+  int32_t k;
+  int32_t rope_cols;       // leading output features rotated, in whole 128-wide heads
+  int32_t tiles_f;
+  int32_t tiles_t;
+  RopeTable tab;
+};
+
 hipError_t launch_rope_qk(const RopeArgs& a, hipStream_t stream);
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_video_pack(const PackArgs& a, hipStream_t stream);
 hipError_t launch_audio_pack(const PackArgs& a, hipStream_t stream);
 hipError_t launch_adaln(const AdalnArgs& a, hipStream_t stream);

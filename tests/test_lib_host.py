@@ -217,3 +217,27 @@ def test_abi_rejects_bad_pack_calls(h3):
     assert vid(t=L + 4096) == E and vid(v=L) == E and vid(t=V + 64) == E   # overlaps
     assert aud(ch=0) == E and aud(s=-1) == E and aud(w=31) == E and aud(w=0) == E
     assert aud(vs=30) == E and aud(ts=33) == E and aud(v=L) == E and aud(t=L) == E
+
+
+def test_abi_rejects_bad_linear_calls(h3):
+    lib = h3.load_library()
+    cfg = h3.rope_cfg()
+    P = 1 << 26
+    X, Wt, B, Y, C = P, 4 * P, 8 * P, 12 * P, 16 * P
+    E, R = h3.H3ATTN_EINVAL, h3.H3ATTN_ERANGE
+
+    def lin(x=X, xs=5376, w=Wt, ws=5376, b=B, y=Y, ys=16128, m=28192, n=16128, k=5376, cf=cfg, c=C, rc=10752):
+        return lib.h3attn_linear(x, xs, w, ws, b, y, ys, m, n, k, ctypes.byref(cf) if cf is not None else None, c, rc,
+                                 None)
+
+    assert lin(m=0) == 0                                     # empty: no-op
+    assert lin(x=None) == E and lin(w=None) == E and lin(y=None) == E
+    assert lin(x=X + 8) == E and lin(y=Y + 2) == E and lin(b=B + 4) == E
+    assert lin(n=16000) == E and lin(k=5370) == E and lin(k=0) == E and lin(n=0) == E and lin(m=-1) == E
+    assert lin(xs=5368) == E and lin(ws=5380) == E and lin(ys=16120) == E
+    assert lin(rc=100) == E and lin(rc=16384) == E and lin(rc=-128) == E
+    assert lin(cf=None) == E and lin(c=None) == E            # rotation without its configuration
+    assert lin(cf=_cfg(h3, head_dim=64)) == E
+    assert lin(y=X + 4096) == E and lin(y=Wt) == E and lin(b=Y + 64) == E   # y overlaps an input
+    assert lin(xs=2 ** 22 + 8) == R                          # a 256-row tile of x spans 2^31 bytes
+    assert lin(m=2 ** 19, xs=5376) == R                      # x spans 2^32 bytes
