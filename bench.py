@@ -3,7 +3,9 @@
 One step = one pass of the whole path over the 5 s 704x1280 packed sequence
 (512 text + 31 x 22 x 40 video + 200 x 2 audio = 28,192 rows, 42 heads x 128):
   h3attn_rope_qk   rotate K by its (t, h, w) coordinates (HBM-bound pass)
-  h3attn_forward   rotate Q in the tile load, then softmax(Q~ K~^T / sqrt(128)) V
+  h3attn_forward_ws  rotate Q in the tile load, then softmax(Q~ K~^T / sqrt(128)) V (the
+                     last, partly filled wave of workgroups split along the keys, with a
+                     caller-owned workspace allocated before the timed region)
 Inputs are seeded synthetic bf16 N(0, 1) tensors, resident in HBM before the
 timed region.  Prints one JSON line.
 
@@ -399,6 +401,8 @@ def main():
     qrot = torch.empty_like(qd) if args.mode == "prerotated" else None
     o = torch.empty_like(qd)
     lse = torch.empty((h, n), dtype=torch.float32, device=dev)
+    ws_bytes = h3.forward_workspace_bytes(n, h)
+    ws = torch.empty(max(ws_bytes, 16) // 4, dtype=torch.float32, device=dev)
     fused = args.mode == "fused"
     # row ranges rotated each step: all rows, or (reusing cached references) text and target rows only
     ranges = [(0, n)]
@@ -426,8 +430,8 @@ def main():
             h3.rope_qk(cfg, coords, qd, qrot, kd, krot, n, h, stride)
         if ev is not None:
             ev[1].record()
-        h3.forward(cfg, coords, 1 if fused else 0, qd if fused else qrot, krot, vd, o, lse, n, h, stride,
-                   stride)
+        h3.forward_ws(cfg, coords, 1 if fused else 0, qd if fused else qrot, krot, vd, o, lse, n, h, stride,
+                      stride, 0.0, ws, ws_bytes)
         if ev is not None:
             ev[2].record()
 
@@ -465,7 +469,7 @@ def main():
                    "tokens_per_s": round(n / (ms_step * 1e-3), 1),
                    "rope_ms": round(rope_ms, 4), "rope_GBps": round(rope_bytes / (rope_ms * 1e-3) / 1e9, 1),
                    "attn_ms": round(attn_ms, 4), "rope_rows": rope_rows,
-                   "reuse_refs": bool(args.reuse_refs)},
+                   "reuse_refs": bool(args.reuse_refs), "workspace_bytes": ws_bytes},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic()},
         "cpu_baseline": cpu,

@@ -273,6 +273,30 @@ int h3attn_audio_euler_pack(float* latent, int32_t n_ch, int32_t steps, int32_t 
                             const void* v_tokens, int64_t v_stride, float dt, void* tokens,
                             int64_t tokens_stride, void* stream);
 
+/*
+ * Device call.  h3attn_forward with a caller-owned scratch workspace (device
+ * memory, 16-byte aligned, not overlapping any tensor argument).  The attention
+ * runs one workgroup per (head, 256-row query block) on each compute unit in
+ * waves; when the last wave would be at most half full, its units are split
+ * along the keys over several workgroups that leave float32 partial results
+ * (unnormalised O and the row's max / sum) in the workspace, merged by a second
+ * kernel with the same max-and-rescale rule.  The result equals h3attn_forward
+ * up to the rounding order of the split rows.  A NULL or too small workspace
+ * runs the unsplit schedule (h3attn_forward); the library still allocates
+ * nothing.  The workspace must not be shared by calls in flight at once.
+ */
+int h3attn_forward_ws(const h3attn_rope_cfg* cfg, const float* coords_dev, int32_t rope_q,
+                      const void* q, const void* k, const void* v, void* o, float* lse,
+                      int64_t n_tokens, int32_t n_heads, int64_t row_stride_qkv,
+                      int64_t row_stride_o, float scale, void* workspace, int64_t workspace_bytes,
+                      void* stream);
+
+/*
+ * Host call.  Workspace bytes h3attn_forward_ws uses for this shape on the
+ * current device (0 when no split pays off, or no gfx950 device is current).
+ */
+int64_t h3attn_forward_workspace_bytes(int64_t n_tokens, int32_t n_heads);
+
 /* Static description of an error code (never NULL). */
 const char* h3attn_strerror(int code);
 

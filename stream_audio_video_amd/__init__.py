@@ -17,6 +17,9 @@ device memory and the current stream.  The functions keep the C names:
   audio_euler_pack(latent, n_ch, steps, width, v_tokens, v_stride, dt, tokens, tokens_stride, stream=None)
   linear(x, x_stride, w, w_stride, bias, y, y_stride, m, n_out, k, rope_cfg=None, coords_dev=None,
          rope_cols=0, stream=None)
+  forward_ws(cfg, coords_dev, rope_q, q, k, v, o, lse, n_tokens, n_heads, row_stride_qkv, row_stride_o,
+             scale, workspace, workspace_bytes, stream=None)
+  forward_workspace_bytes(n_tokens, n_heads)
   strerror(code), version()
 
 Tensor arguments may be torch tensors (their data_ptr is passed) or raw
@@ -37,7 +40,7 @@ ADALN_MAX_HIDDEN = 8192
 
 EXPORTED = ("h3attn_build_coords", "h3attn_rope_qk", "h3attn_forward", "h3attn_adaln_modulate",
             "h3attn_adaln_residual", "h3attn_video_euler_pack", "h3attn_audio_euler_pack", "h3attn_strerror",
-            "h3attn_linear", "h3attn_version")
+            "h3attn_linear", "h3attn_forward_ws", "h3attn_forward_workspace_bytes", "h3attn_version")
 
 
 class H3AttnError(RuntimeError):
@@ -90,6 +93,11 @@ def load_library(path=None):
     lib.h3attn_linear.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, i32, i32, ctypes.POINTER(RopeCfg), vp, i32,
                                   vp]
     lib.h3attn_linear.restype = ctypes.c_int
+    lib.h3attn_forward_ws.argtypes = [ctypes.POINTER(RopeCfg), vp, i32, vp, vp, vp, vp, vp, i64, i32, i64, i64,
+                                      ctypes.c_float, vp, i64, vp]
+    lib.h3attn_forward_ws.restype = ctypes.c_int
+    lib.h3attn_forward_workspace_bytes.argtypes = [i64, i32]
+    lib.h3attn_forward_workspace_bytes.restype = i64
     lib.h3attn_strerror.argtypes = [ctypes.c_int]
     lib.h3attn_strerror.restype = ctypes.c_char_p
     lib.h3attn_version.argtypes = []
@@ -210,6 +218,20 @@ def linear(x, x_stride, w, w_stride, bias, y, y_stride, m, n_out, k, rope_cfg=No
                             _ptr(coords_dev), int(rope_cols), _stream(stream))
     if rc != H3ATTN_OK:
         raise H3AttnError("h3attn_linear", rc)
+
+
+def forward_ws(cfg, coords_dev, rope_q, q, k, v, o, lse, n_tokens, n_heads, row_stride_qkv, row_stride_o, scale,
+               workspace, workspace_bytes, stream=None):
+    rc = _L().h3attn_forward_ws(ctypes.byref(cfg), _ptr(coords_dev), int(rope_q), _ptr(q), _ptr(k), _ptr(v),
+                                _ptr(o), _ptr(lse), int(n_tokens), int(n_heads), int(row_stride_qkv),
+                                int(row_stride_o), float(scale), _ptr(workspace), int(workspace_bytes),
+                                _stream(stream))
+    if rc != H3ATTN_OK:
+        raise H3AttnError("h3attn_forward_ws", rc)
+
+
+def forward_workspace_bytes(n_tokens, n_heads):
+    return int(_L().h3attn_forward_workspace_bytes(int(n_tokens), int(n_heads)))
 
 
 def mmrope_attention(q, k, v, coords_dev, cfg=None, scale=0.0, want_lse=True, fuse_q=True, k_rot=None,

@@ -116,8 +116,20 @@ __global__ __launch_bounds__(kThreads, kQB == 1 ? 2 : 1) void attn_fwd_kernel(Fw
   const int col = lane & 31;   // query column / A-operand row of this lane
   const int hf = lane >> 5;    // which 8-element half of a 16-deep k chunk
   const int nqb = (a.n + kBM - 1) / kBM;
-  const int head = blockIdx.x / nqb;
-  const int qblk = blockIdx.x - head * nqb;
+  const int ntiles = (a.n + kBN - 1) / kBN;
+  // work unit = (head, query block).  The first n_full workgroups take one unit each over all
+  // keys; each later unit is split over `split` workgroups, part p taking key tiles
+  // [p * tiles_per_split, ...), and leaves an unnormalised partial result for the merge.
+  int unit = blockIdx.x, part = -1, t_begin = 0, t_end = ntiles;
+  if (unit >= a.n_full) {
+    const int r = unit - a.n_full;
+    unit = a.n_full + r / a.split;
+    part = r - (r / a.split) * a.split;
+    t_begin = part * a.tiles_per_split;
+    t_end = min(t_begin + a.tiles_per_split, ntiles);
+  }
+  const int head = unit / nqb;
+  const int qblk = unit - head * nqb;
   const float qscale = a.scale_log2;
 
   // ---- Q~ fragments: B operand of S^T; lane holds dims 16c + 8hf .. +7 of its query
@@ -348,26 +360,47 @@ __global__ __launch_bounds__(kThreads, kQB == 1 ? 2 : 1) void attn_fwd_kernel(Fw
     pv(t & 1, pb);
   };
 
-  // Double-buffered tiles, one barrier per tile: tile t+1 is loaded into
-  // registers while tile t is computed, then stored into the other buffer.
-  const int ntiles = (a.n + kBN - 1) / kBN;
-  load_tile(0);
-  store_tile(0);
+  // Double-buffered tiles over [t_begin, t_end), one barrier per tile: tile t+1 is loaded into
+  // registers while tile t is computed, then stored into the other buffer (tile t uses buffer
+  // t & 1).  The last step masks keys >= n, which only bites on the sequence's last tile.
+  load_tile(t_begin);
+  store_tile(t_begin & 1);
   __syncthreads();
-  if (ntiles == 1) {
-    step(0, True{}, True{});
+  if (t_end - t_begin == 1) {
+    step(t_begin, True{}, True{});
   } else {
-    load_tile(1);
-    step(0, True{}, False{});
-    store_tile(1);
-    for (int t = 1; t + 1 < ntiles; ++t) {
+    load_tile(t_begin + 1);
+    step(t_begin, True{}, False{});
+    store_tile((t_begin + 1) & 1);
+    for (int t = t_begin + 1; t + 1 < t_end; ++t) {
       __syncthreads();
       load_tile(t + 1);
       step(t, False{}, False{});
       store_tile((t + 1) & 1);
     }
     __syncthreads();
-    step(ntiles - 1, False{}, True{});
+    step(t_end - 1, False{}, True{});
+  }
+
+  if (part >= 0) {
+    // partial result of one key range: O^T unnormalised (float32) and (m, l) per query row
+    const int slot = blockIdx.x - a.n_full;
+#pragma unroll
+    for (int i = 0; i < kQB; ++i) {
+      const float l_tot = pair_sum(l_part[i]);
+      const int rloc = (wave * kQB + i) * 32 + col;
+      float* po = a.ws_o + (int64_t(slot) * kBM + rloc) * kHeadDim;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          *reinterpret_cast<float4*>(po + 32 * db + 8 * r + 4 * hf) =
+              make_float4(oacc[i][db][4 * r + 0], oacc[i][db][4 * r + 1], oacc[i][db][4 * r + 2],
+                          oacc[i][db][4 * r + 3]);
+      if (hf == 0)
+        *reinterpret_cast<float2*>(a.ws_ml + (int64_t(slot) * kBM + rloc) * 2) = make_float2(m_ref[i], l_tot);
+    }
+    return;
   }
 
   // ---- epilogue: O = O^T / l, LSE = (m + log2 l) * ln 2
@@ -392,13 +425,81 @@ __global__ __launch_bounds__(kThreads, kQB == 1 ? 2 : 1) void attn_fwd_kernel(Fw
   }
 }
 
+// Merge of the key-range partials of split units: per query row, with m = max_p m_p and
+// w_p = 2^(m_p - m), O = sum_p w_p O_p / sum_p w_p l_p and LSE = (m + log2 sum_p w_p l_p) ln 2.
+// Block: 8 rows x 16 lanes of 8 head-dim values; grid (rows / 8, split units).
+__global__ __launch_bounds__(128) void attn_merge_kernel(FwdArgs a) {
+  const int nqb = (a.n + kBM - 1) / kBM;
+  const int su = blockIdx.y;                               // split unit
+  const int unit = a.n_full + su;
+  const int head = unit / nqb, qblk = unit - head * nqb;
+  const int rloc = blockIdx.x * 8 + (threadIdx.x >> 4), d0 = 8 * (threadIdx.x & 15);
+  const int row = qblk * kBM + rloc;
+  if (row >= a.n) return;
+  float m = -__builtin_inff();
+  for (int p = 0; p < a.split; ++p) m = fmaxf(m, a.ws_ml[(int64_t(su * a.split + p) * kBM + rloc) * 2]);
+  float l = 0.0f, o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int p = 0; p < a.split; ++p) {
+    const int64_t slot = int64_t(su * a.split + p) * kBM + rloc;
+    const float2 ml = *reinterpret_cast<const float2*>(a.ws_ml + slot * 2);
+    const float w = __builtin_amdgcn_exp2f(ml.x - m);
+    l = __builtin_fmaf(w, ml.y, l);
+    const float4 x0 = *reinterpret_cast<const float4*>(a.ws_o + slot * kHeadDim + d0);
+    const float4 x1 = *reinterpret_cast<const float4*>(a.ws_o + slot * kHeadDim + d0 + 4);
+    o[0] = __builtin_fmaf(w, x0.x, o[0]); o[1] = __builtin_fmaf(w, x0.y, o[1]);
+    o[2] = __builtin_fmaf(w, x0.z, o[2]); o[3] = __builtin_fmaf(w, x0.w, o[3]);
+    o[4] = __builtin_fmaf(w, x1.x, o[4]); o[5] = __builtin_fmaf(w, x1.y, o[5]);
+    o[6] = __builtin_fmaf(w, x1.z, o[6]); o[7] = __builtin_fmaf(w, x1.w, o[7]);
+  }
+  const float inv = 1.0f / l;
+  uint4 out;
+  out.x = pack_bf16x2(o[0] * inv, o[1] * inv);
+  out.y = pack_bf16x2(o[2] * inv, o[3] * inv);
+  out.z = pack_bf16x2(o[4] * inv, o[5] * inv);
+  out.w = pack_bf16x2(o[6] * inv, o[7] * inv);
+  *reinterpret_cast<uint4*>(a.o + int64_t(row) * a.stride_o + head * kHeadDim + d0) = out;
+  if (a.lse != nullptr && d0 == 0) a.lse[head * a.n + row] = (m + __log2f(l)) * 0.69314718055994531f;
+}
+
 }  // namespace
 
 hipError_t launch_attn_fwd(const FwdArgs& a, hipStream_t stream) {
   const int nqb = (a.n + kBM - 1) / kBM;
-  const dim3 grid(nqb * a.heads), block(kThreads);
-  void* args[] = {const_cast<FwdArgs*>(&a)};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_kernel), grid, block, args, 0, stream);
+  const int units = nqb * a.heads;
+  const int split_units = units - a.n_full;
+  const dim3 grid(a.n_full + split_units * a.split), block(kThreads);
+  FwdArgs b = a;
+  if (split_units > 0) b.ws_ml = b.ws_o + int64_t(split_units) * a.split * kBM * kHeadDim;
+  void* args[] = {&b};
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_kernel), grid, block, args, 0, stream);
+  if (e != hipSuccess || split_units == 0) return e;
+  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_merge_kernel), dim3(kBM / 8, split_units), dim3(128),
+                         args, 0, stream);
+}
+
+void attn_fwd_schedule(int32_t n, int32_t heads, int32_t cus, int32_t* n_full, int32_t* split,
+                       int32_t* tiles_per_split, int64_t* ws_bytes) {
+  const int nqb = (n + kBM - 1) / kBM;
+  const int ntiles = (n + kBN - 1) / kBN;
+  const int units = nqb * heads;
+  *n_full = units;
+  *split = 1;
+  *tiles_per_split = ntiles;
+  *ws_bytes = 0;
+  // only a last wave of workgroups filled to at most half is worth splitting (one workgroup per CU)
+  const int rem = cus > 0 ? units % cus : 0;
+  if (units < cus || rem == 0 || 2 * rem > cus || ntiles < 8) return;
+  int s = cus / rem;
+  s = s < 2 ? 2 : (s > 8 ? 8 : s);
+  if (s > ntiles / 4) s = ntiles / 4;
+  if (s < 2) return;
+  const int tps = (ntiles + s - 1) / s;
+  s = (ntiles + tps - 1) / tps;                       // every part non-empty
+  if (s < 2) return;
+  *n_full = units - rem;
+  *split = s;
+  *tiles_per_split = tps;
+  *ws_bytes = int64_t(rem) * s * kBM * (kHeadDim + 2) * 4;
 }
 
 }  // namespace h3

@@ -95,10 +95,61 @@ extern "C" int h3attn_rope_qk(const h3attn_rope_cfg* cfg, const float* coords_de
                                                                                : H3ATTN_EHIP;
 }
 
+namespace {
+
+std::atomic<int> g_device_cus[kMaxDevices];
+
+// compute units of the current device (cached), or 0 when it cannot be read
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int cus = g_device_cus[dev].load(std::memory_order_relaxed);
+  if (cus == 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    g_device_cus[dev].store(cus, std::memory_order_relaxed);
+  }
+  return cus;
+}
+
+int forward_impl(const h3attn_rope_cfg* cfg, const float* coords_dev, int32_t rope_q, const void* q, const void* k,
+                 const void* v, void* o, float* lse, int64_t n_tokens, int32_t n_heads, int64_t row_stride_qkv,
+                 int64_t row_stride_o, float scale, void* workspace, int64_t workspace_bytes, void* stream);
+
+}  // namespace
+
+extern "C" int64_t h3attn_forward_workspace_bytes(int64_t n_tokens, int32_t n_heads) {
+  if (n_tokens <= 0 || n_heads <= 0 || n_tokens >= (int64_t(1) << 31)) return 0;
+  if (check_device() != H3ATTN_OK) return 0;
+  int32_t n_full, split, tps;
+  int64_t bytes;
+  h3::attn_fwd_schedule(static_cast<int32_t>(n_tokens), n_heads, device_cus(), &n_full, &split, &tps, &bytes);
+  return bytes;
+}
+
 extern "C" int h3attn_forward(const h3attn_rope_cfg* cfg, const float* coords_dev, int32_t rope_q,
                               const void* q, const void* k, const void* v, void* o, float* lse,
                               int64_t n_tokens, int32_t n_heads, int64_t row_stride_qkv,
                               int64_t row_stride_o, float scale, void* stream) {
+  return forward_impl(cfg, coords_dev, rope_q, q, k, v, o, lse, n_tokens, n_heads, row_stride_qkv, row_stride_o,
+                      scale, nullptr, 0, stream);
+}
+
+extern "C" int h3attn_forward_ws(const h3attn_rope_cfg* cfg, const float* coords_dev, int32_t rope_q,
+                                 const void* q, const void* k, const void* v, void* o, float* lse,
+                                 int64_t n_tokens, int32_t n_heads, int64_t row_stride_qkv,
+                                 int64_t row_stride_o, float scale, void* workspace, int64_t workspace_bytes,
+                                 void* stream) {
+  if (workspace_bytes < 0 || (workspace != nullptr && (reinterpret_cast<uintptr_t>(workspace) & 15u) != 0))
+    return H3ATTN_EINVAL;
+  return forward_impl(cfg, coords_dev, rope_q, q, k, v, o, lse, n_tokens, n_heads, row_stride_qkv, row_stride_o,
+                      scale, workspace, workspace_bytes, stream);
+}
+
+namespace {
+
+int forward_impl(const h3attn_rope_cfg* cfg, const float* coords_dev, int32_t rope_q, const void* q, const void* k,
+                 const void* v, void* o, float* lse, int64_t n_tokens, int32_t n_heads, int64_t row_stride_qkv,
+                 int64_t row_stride_o, float scale, void* workspace, int64_t workspace_bytes, void* stream) {
   h3::FwdArgs a;
   std::memset(&a, 0, sizeof(a));
   int rc = make_table(cfg, &a.tab);
@@ -135,9 +186,26 @@ extern "C" int h3attn_forward(const h3attn_rope_cfg* cfg, const float* coords_de
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.rope_q = rope_q ? 1 : 0;
+  // the key-split tail runs only with a workspace that holds its partials, disjoint from the tensors
+  int64_t ws_need = 0;
+  h3::attn_fwd_schedule(a.n, a.heads, workspace != nullptr ? device_cus() : 0, &a.n_full, &a.split,
+                        &a.tiles_per_split, &ws_need);
+  if (ws_need > 0 && (workspace_bytes < ws_need || overlaps(workspace, ws_need, o, out_bytes) ||
+                      overlaps(workspace, ws_need, q, in_bytes) || overlaps(workspace, ws_need, k, in_bytes) ||
+                      overlaps(workspace, ws_need, v, in_bytes) ||
+                      (lse != nullptr && overlaps(workspace, ws_need, lse, int64_t(n_heads) * n_tokens * 4)))) {
+    if (workspace_bytes < ws_need) {
+      h3::attn_fwd_schedule(a.n, a.heads, 0, &a.n_full, &a.split, &a.tiles_per_split, &ws_need);
+    } else {
+      return H3ATTN_EINVAL;
+    }
+  }
+  if (ws_need > 0) a.ws_o = static_cast<float*>(workspace);   // the launcher lays out the partials
   return h3::launch_attn_fwd(a, static_cast<hipStream_t>(stream)) == hipSuccess ? H3ATTN_OK
                                                                                 : H3ATTN_EHIP;
 }
+
+}  // namespace
 
 namespace {
 

@@ -35,7 +35,11 @@ struct FwdArgs {
   float scale;         // softmax scale (natural base)
   float scale_log2;    // scale * log2(e)
   int32_t rope_q;
-  int32_t pad_;
+  int32_t n_full;          // work units (head, query block) run over all keys, one workgroup each
+  int32_t split;           // key ranges per later unit (1: no later units)
+  int32_t tiles_per_split; // key tiles per range
+  float* ws_o;             // partials of split units: float32 [unit * split + part][rows][128]
+  float* ws_ml;            // and their (m, l) per row: float32 [unit * split + part][rows][2]
   RopeTable tab;
 };
 
@@ -98,5 +102,9 @@ hipError_t launch_video_pack(const PackArgs& a, hipStream_t stream);
 hipError_t launch_audio_pack(const PackArgs& a, hipStream_t stream);
 hipError_t launch_adaln(const AdalnArgs& a, hipStream_t stream);
 hipError_t launch_attn_fwd(const FwdArgs& a, hipStream_t stream);
+// Key-split schedule of the last, partly filled wave of attention workgroups on `cus` CUs:
+// fills n_full, split, tiles_per_split and the workspace bytes it needs (0: no split).
+void attn_fwd_schedule(int32_t n, int32_t heads, int32_t cus, int32_t* n_full, int32_t* split,
+                       int32_t* tiles_per_split, int64_t* ws_bytes);
 
 }  // namespace h3
