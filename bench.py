@@ -355,6 +355,8 @@ def main():
     ap.add_argument("--mode", default="fused", choices=["fused", "prerotated"])
     ap.add_argument("--reuse-refs", action="store_true",
                     help="keep the reference rows' rotated K cached across steps; rotate only text and target rows")
+    ap.add_argument("--no-split", action="store_true",
+                    help="attention without a workspace: the last, partly filled wave is not split along the keys")
     ap.add_argument("--path", default="attention", choices=["attention", "adaln", "pack", "qkv"],
                     help="attention: MM-RoPE + attention (the headline); adaln: the AdaLN residual row")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing (0 = skip)")
@@ -401,7 +403,7 @@ def main():
     qrot = torch.empty_like(qd) if args.mode == "prerotated" else None
     o = torch.empty_like(qd)
     lse = torch.empty((h, n), dtype=torch.float32, device=dev)
-    ws_bytes = h3.forward_workspace_bytes(n, h)
+    ws_bytes = 0 if args.no_split else h3.forward_workspace_bytes(n, h)
     ws = torch.empty(max(ws_bytes, 16) // 4, dtype=torch.float32, device=dev)
     fused = args.mode == "fused"
     # row ranges rotated each step: all rows, or (reusing cached references) text and target rows only
