@@ -48,6 +48,8 @@ ATTN_SOURCE = os.path.join(CSRC, "attn_fwd.hip")
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "attn_fwd_5s_hbm_traffic.json")
 ADALN_SOURCE = os.path.join(CSRC, "adaln_kernel.hip")
 ADALN_TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "adaln_residual_5s_hbm_traffic.json")
+GEMM_SOURCE = os.path.join(CSRC, "gemm_kernel.hip")
+QKV_TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "linear_qkv_5s_hbm_traffic.json")
 
 
 def measured_traffic(record=TRAFFIC_RECORD, source=ATTN_SOURCE, key="attn_fwd_sha256"):
@@ -340,7 +342,9 @@ def bench_qkv(args):
                    "qkv_ms": round(qkv_ms, 4), "qkv_TFLOPs": round(achieved, 2), "out_proj_ms": round(out_ms, 4),
                    "out_proj_TFLOPs": round(flop_out / (out_ms * 1e-3) / 1e12, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": (measured_traffic(QKV_TRAFFIC_RECORD, GEMM_SOURCE, "gemm_sha256")
+                                 if args.config == "5s" else None)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

@@ -14,14 +14,31 @@
 // and, in consecutive accumulator registers, consecutive output features: the
 // rotation pairs (2p, 2p + 1) of a head are neighbouring registers of one lane.
 //
-// A workgroup of 8 waves computes 256 features x 256 tokens; wave (wf, wt) owns
-// features [128 wf, +128) (one whole head) and tokens [64 wt, +64).  k advances
-// 64 at a time through double-buffered LDS tiles whose 144-byte rows make the
-// 16-byte operand reads bank-conflict-free; the next stage's global loads are in
-// flight while the current one is multiplied.  Workgroups are ordered in groups
-// of 8 token tiles so that the tiles in flight share x and W in the caches.
-// Rows of x past m read as zero (buffer loads with a clamped descriptor) and
-// their outputs are not stored.
+// A workgroup of 4 waves (one per SIMD) computes 256 features x 256 tokens;
+// wave (wf, wt) owns features [128 wf, +128) (one whole head) and tokens
+// [128 wt, +128): 16 accumulator blocks (in AGPRs), so every 16-byte LDS operand
+// read feeds four MFMAs.  k advances 64 at a time through two LDS stages filled
+// by direct-to-LDS buffer loads (no staging registers).  Each wave load
+// instruction writes 1 KB = 8 rows of 128 B, and a row's 16-byte chunk c is
+// stored at slot c ^ ((row >> 1) & 7), which keeps the operand reads of 16 rows
+// on disjoint banks.
+//
+// Schedule.  With one wave per SIMD nothing else hides a wave's own stalls, so
+// every MFMA is followed by at most one other memory instruction: in each
+// k-step of 16 MFMAs, MFMAs 0..7 each cover one operand read of the next k-step
+// and MFMAs 8..15 each cover one load of a later stage.  The barrier of stage s
+// sits before its last k-step, whose MFMAs then hide the reads of the next
+// stage's first k-step.  Workgroups are ordered in groups of kGroup token tiles
+// so that the tiles in flight share x and W in the caches.  Rows of x past m
+// read as zero (clamped buffer descriptor) and their outputs are not stored.
+//
+// The loads are written in inline assembly: issued through the compiler's
+// buffer-to-LDS builtin, every operand read of one stage would wait for the
+// loads in flight into the other stage (the compiler cannot tell the two LDS
+// stages apart), which serialises the pipeline.  The assembly has no register
+// outputs; it sets M0 (the LDS destination), which no compiler-generated
+// instruction of this kernel uses on gfx950, and the waits for the loads are
+// explicit (vmcnt(0) before each barrier; none is outstanding at the epilogue).
 #include "launch.hpp"
 
 namespace h3 {
@@ -29,29 +46,53 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8;
-typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
 
-constexpr int kWaves = 8;
+constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 256;                    // features and tokens per workgroup
-constexpr int kBK = 64;                       // k per stage
-constexpr int kStr = kBK + 8;                 // LDS row stride, elements (144 B)
-constexpr int kBuf = kTile * kStr;            // elements per operand buffer
-constexpr int kLoads = kTile * kBK / 8 / kThreads;   // 16-byte chunks per thread, operand and stage (4)
-constexpr int kGroup = 8;                     // token tiles per ordering group
+constexpr int kBK = 64;                       // k per stage (128 B per row)
+constexpr int kBuf = kTile * kBK;             // elements per operand stage
+constexpr int kRowsPerWave = kTile / kWaves;  // rows of each operand a wave loads per stage (64)
+constexpr int kEarly = 8;                     // loads of a stage issued as soon as its buffer is free
+constexpr int kGroup = 4;                     // token tiles per ordering group
 constexpr int kRsrcFlags = 0x00020000;        // raw buffer, 32-bit data format
+static_assert(kEarly >= 0 && kEarly <= 8, "at most one load per MFMA");
+
+struct True { static constexpr bool value = true; };
+struct False { static constexpr bool value = false; };
 
 __device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t as[2 * kBuf];   // W tile [feature][k]
-  __shared__ __attribute__((aligned(16))) uint16_t bs[2 * kBuf];   // x tile [token][k]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 31, hf = lane >> 5;
+// raw buffer descriptor in scalar registers: base, no stride, `bytes` readable
+__device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  i32x4_t r;
+  r[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(p)));
+  r[1] = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(p >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
+  r[3] = kRsrcFlags;
+  return r;
+}
+
+// 16 bytes per lane from buffer offset voff + soff into LDS at lds_addr + 16 * lane.  M0 carries
+// the LDS address; one wait state separates its write from the load.
+__device__ __forceinline__ void load_lds(i32x4_t rsrc, int voff, uint32_t lds_addr, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+}
+
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0f70); }   // vmcnt(0)
+
+__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint16_t as[2 * kBuf];   // W stages [feature][k], swizzled
+  __shared__ __attribute__((aligned(1024))) uint16_t bs[2 * kBuf];   // x stages [token][k], swizzled
+  const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, hf = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wf = wave & 1, wt = wave >> 1;
 
   // grouped tile order: kGroup token tiles sweep all feature tiles together
@@ -64,88 +105,113 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a) {
   const int tf = in_group / gsz;
   const int f0 = tf * kTile, t0 = tt * kTile;
 
-  // global -> register staging: chunk q = tid + kThreads i is row q / 8, k columns 8 (q % 8) ..
+  // direct-to-LDS loads: instruction i of this wave fills rows 64 wave + 8 i .. +7 (1 KB); lane l
+  // writes slot l & 7 of row 64 wave + 8 i + (l >> 3), which holds source chunk
+  // (l & 7) ^ ((row >> 1) & 7) = (l & 7) ^ ((4 i + (l >> 4)) & 7).  The stage's k offset goes in
+  // the scalar offset.
   const int xrow_bytes = static_cast<int>(a.x_stride * 2), wrow_bytes = static_cast<int>(a.w_stride * 2);
   const int64_t x_left = (int64_t(a.m) - t0) * a.x_stride * 2;
-  const __amdgpu_buffer_rsrc_t xd = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.x + int64_t(t0) * a.x_stride), 0, static_cast<int>(static_cast<uint32_t>(x_left)), kRsrcFlags);
-  const __amdgpu_buffer_rsrc_t wd = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.w + int64_t(f0) * a.w_stride), 0, kTile * wrow_bytes, kRsrcFlags);
-  int xoff[kLoads], woff[kLoads], lds_st[kLoads];
+  const i32x4_t xd = make_rsrc(a.x + int64_t(t0) * a.x_stride, static_cast<uint32_t>(x_left));
+  const i32x4_t wd = make_rsrc(a.w + int64_t(f0) * a.w_stride, static_cast<uint32_t>(kTile * wrow_bytes));
+  const int lrow = lane >> 3, lpos = lane & 7;
+  int voff[16];
 #pragma unroll
-  for (int i = 0; i < kLoads; ++i) {
-    const int q = tid + kThreads * i, row = q >> 3, c8 = q & 7;
-    xoff[i] = row * xrow_bytes + c8 * 16;
-    woff[i] = row * wrow_bytes + c8 * 16;
-    lds_st[i] = row * kStr + c8 * 8;
+  for (int j = 0; j < 16; ++j) {
+    const int i = j & 7;
+    const int c = lpos ^ ((4 * i + (lane >> 4)) & 7);
+    const int rb = j < 8 ? wrow_bytes : xrow_bytes;
+    voff[j] = (kRowsPerWave * wave + 8 * i + lrow) * rb + c * 16;
   }
-  u32x4_t xr[kLoads], wr[kLoads];
-  auto load = [&](int s) {
-    const int kb = s * kBK * 2;
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      wr[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wd, woff[i] + kb, 0, 0));
-      xr[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xd, xoff[i] + kb, 0, 0));
-    }
-  };
-  lds_u16* asl = (lds_u16*)as;
-  lds_u16* bsl = (lds_u16*)bs;
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      *reinterpret_cast<lds_u32x4*>(asl + buf * kBuf + lds_st[i]) = wr[i];
-      *reinterpret_cast<lds_u32x4*>(bsl + buf * kBuf + lds_st[i]) = xr[i];
-    }
+  const uint32_t as_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_u16*)as));
+  const uint32_t bs_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_u16*)bs));
+  // load j = 0..15 of stage s into buffer buf: j < 8 are W rows, j >= 8 are x rows
+  auto load_one = [&](int s, int buf, int j) {
+    const int i = j & 7;
+    const uint32_t lds = (j < 8 ? as_addr : bs_addr) +
+                         static_cast<uint32_t>((buf * kBuf + (kRowsPerWave * wave + 8 * i) * kBK) * 2);
+    load_lds(j < 8 ? wd : xd, voff[j], __builtin_amdgcn_readfirstlane(lds), s * kBK * 2);
   };
 
-  // operand reads: A (W) rows 128 wf + 32 fb + col, B (x) rows 64 wt + 32 tb + col, k 16 kk + 8 hf
-  const int a_rd = (wf * 128 + col) * kStr + 8 * hf;
-  const int b_rd = (wt * 64 + col) * kStr + 8 * hf;
-  f32x16_t acc[4][2];
+  // operand reads: A rows 128 wf + 32 fb + col, B rows 128 wt + 32 tb + col; chunk 2 kk + hf.
+  const int a_row = wf * 128 + col, b_row = wt * 128 + col;
+  const int a_sw = (a_row >> 1) & 7, b_sw = (b_row >> 1) & 7;
+  const lds_u16* asl = (const lds_u16*)as;
+  const lds_u16* bsl = (const lds_u16*)bs;
+  f32x16_t acc[4][4];
 #pragma unroll
   for (int fb = 0; fb < 4; ++fb)
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) acc[fb][tb] = f32x16_t{};
+    for (int tb = 0; tb < 4; ++tb) acc[fb][tb] = f32x16_t{};
 
-  auto compute = [&](int buf) {
-    const lds_u16* at = asl + buf * kBuf + a_rd;
-    const lds_u16* bt = bsl + buf * kBuf + b_rd;
-    bf16x8_t af[2][4], bf[2][2];
-    auto read = [&](int kk, int slot) {
+  bf16x8_t op[2][8];   // [slot][0..3 = A fb, 4..7 = B tb]
+  auto read_one = [&](int buf, int kk, int slot, int e) {
+    if (e < 4)
+      op[slot][e] = *reinterpret_cast<const lds_bf16x8*>(asl + buf * kBuf + (a_row + 32 * e) * kBK +
+                                                         ((2 * kk + hf) ^ a_sw) * 8);
+    else
+      op[slot][e] = *reinterpret_cast<const lds_bf16x8*>(bsl + buf * kBuf + (b_row + 32 * (e - 4)) * kBK +
+                                                         ((2 * kk + hf) ^ b_sw) * 8);
+  };
+
+  // One k-step: 16 MFMAs on operand slot `slot`.  After MFMA q < 8 read operand q of k-step rkk
+  // of buffer rbuf into the other slot (if do_read); after MFMA q >= 8 issue load j0 + q - 8 of
+  // stage lstage into buffer lbuf (if q - 8 < nload).  The scheduling barriers keep that order.
+  auto kstep = [&](int slot, bool do_read, int rbuf, int rkk, int nload, int lstage, int lbuf, int j0) {
 #pragma unroll
-      for (int fb = 0; fb < 4; ++fb) af[slot][fb] = *reinterpret_cast<const lds_bf16x8*>(at + fb * 32 * kStr + 16 * kk);
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) bf[slot][tb] = *reinterpret_cast<const lds_bf16x8*>(bt + tb * 32 * kStr + 16 * kk);
-    };
-    read(0, 0);
-#pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      if (kk + 1 < kBK / 16) read(kk + 1, (kk + 1) & 1);
-#pragma unroll
-      for (int fb = 0; fb < 4; ++fb)
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb) acc[fb][tb] = mfma(af[kk & 1][fb], bf[kk & 1][tb], acc[fb][tb]);
+    for (int q = 0; q < 16; ++q) {
+      const int fb = q >> 2, tb = q & 3;
+      acc[fb][tb] = mfma(op[slot][fb], op[slot][4 + tb], acc[fb][tb]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (q < 8) {
+        if (do_read) read_one(rbuf, rkk, slot ^ 1, q);
+      } else if (q - 8 < nload) {
+        load_one(lstage, lbuf, j0 + q - 8);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
+  // Stage s lives in buffer s & 1.  Loads of stage s + 1: the W half (loads 0..7) right after the
+  // barrier that frees its buffer (during k-step 3 of stage s - 1), the x half during k-step 0 of
+  // stage s; all land before the barrier ahead of k-step 3 of stage s.
   const int nst = a.k / kBK;
-  load(0);
-  store(0);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) load_one(0, 0, j);
+  wait_vm0();
   __syncthreads();
-  if (nst > 1) load(1);
-  for (int s = 0; s < nst; ++s) {
-    compute(s & 1);
-    if (s + 1 < nst) store((s + 1) & 1);
-    if (s + 2 < nst) load(s + 2);
-    __syncthreads();
+  if (nst > 1) {
+#pragma unroll
+    for (int j = 0; j < kEarly; ++j) load_one(1, 1, j);
   }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) read_one(0, 0, 0, e);
+  // one stage; more1 / more2: stages s + 1 / s + 2 exist (compile-time, so the steady state has no
+  // branches)
+  auto stage = [&](int s, auto more1_t, auto more2_t) {
+    constexpr bool more1 = decltype(more1_t)::value, more2 = decltype(more2_t)::value;
+    const int buf = s & 1;
+    kstep(0, true, buf, 1, more1 ? 16 - kEarly : 0, s + 1, buf ^ 1, kEarly);
+    __builtin_amdgcn_sched_barrier(0);
+    kstep(1, true, buf, 2, 0, 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    kstep(0, true, buf, 3, 0, 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm0();        // this wave's loads of stage s + 1 are in LDS
+    __syncthreads();   // ... and every wave's; every wave is done reading stage s's buffer
+    kstep(1, more1, buf ^ 1, 0, more2 ? kEarly : 0, s + 2, buf, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  int s = 0;
+  for (; s + 2 < nst; ++s) stage(s, True{}, True{});
+  if (s + 1 < nst) stage(s++, True{}, False{});
+  stage(s, False{}, False{});
 
   // epilogue: bias, rotation of whole-head slabs, one rounding to bf16
   const int fw0 = f0 + wf * 128;                       // first feature of this wave: a head boundary
   const bool rotate = fw0 < a.rope_cols;
 #pragma unroll
-  for (int tb = 0; tb < 2; ++tb) {
-    const int token = t0 + wt * 64 + tb * 32 + col;
+  for (int tb = 0; tb < 4; ++tb) {
+    const int token = t0 + wt * 128 + tb * 32 + col;
     const bool valid = token < a.m;
     float pos0 = 0.0f, pos1 = 0.0f, pos2 = 0.0f;
     if (rotate && valid) {
