@@ -91,6 +91,19 @@ def test_qkv_projection_with_rope(gpu_lib, m):
     check(y, ref, f64(x), f64(w), f64(b), 2 * heads * 128, "qkv m=%d" % m)
 
 
+@pytest.mark.parametrize("k", [64, 128, 192, 320])
+def test_short_reductions(gpu_lib, k):
+    """One to five 64-deep k stages: the pipeline's first and last stages without a steady state."""
+    m, heads = 287, 1
+    n = 3 * heads * 128 + 128                     # Q, K, V of one head plus one more 128-wide block
+    x, w, b = W.projection_inputs(m, k, n, seed=k)
+    coords_h = gpu_lib.build_coords(segs_of(m))
+    y = run(gpu_lib, x, w, b, m, n, k, 2 * heads * 128, torch.from_numpy(coords_h).cuda(), x_stride=k + 8)
+    yr = linear(f64(x), f64(w), f64(b))
+    yr[:, :256] = qkv_rope(f64(x), f64(w[:384]), f64(b[:384]), coords_h, heads, SEC, TH)[:, :256]
+    check(y, yr, f64(x), f64(w), f64(b), 2 * heads * 128, "k=%d" % k)
+
+
 def test_plain_projection_and_strides(gpu_lib):
     m, k, n = 257, 1024, 512
     x, w, _ = W.projection_inputs(m, k, n, seed=3, with_bias=False)
