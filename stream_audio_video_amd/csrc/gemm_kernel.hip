@@ -24,9 +24,9 @@
 // on disjoint banks.
 //
 // Schedule.  With one wave per SIMD nothing else hides a wave's own stalls, so
-// every MFMA is followed by at most one other memory instruction: in each
+// every MFMA is followed by at most two other memory instructions: in each
 // k-step of 16 MFMAs, MFMAs 0..7 each cover one operand read of the next k-step
-// and MFMAs 8..15 each cover one load of a later stage.  The barrier of stage s
+// and every odd MFMA covers one load of a later stage.  The barrier of stage s
 // sits before its last k-step, whose MFMAs then hide the reads of the next
 // stage's first k-step.  Workgroups are ordered in groups of kGroup token tiles
 // so that the tiles in flight share x and W in the caches.  Rows of x past m
@@ -154,19 +154,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs a) {
   };
 
   // One k-step: 16 MFMAs on operand slot `slot`.  After MFMA q < 8 read operand q of k-step rkk
-  // of buffer rbuf into the other slot (if do_read); after MFMA q >= 8 issue load j0 + q - 8 of
-  // stage lstage into buffer lbuf (if q - 8 < nload).  The scheduling barriers keep that order.
+  // of buffer rbuf into the other slot (if do_read); after each odd MFMA q issue load
+  // j0 + (q >> 1) of stage lstage into buffer lbuf (if (q >> 1) < nload), so that the four waves'
+  // loads reach the memory pipeline spread out rather than in bursts.  The scheduling barriers
+  // keep that order.
   auto kstep = [&](int slot, bool do_read, int rbuf, int rkk, int nload, int lstage, int lbuf, int j0) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const int fb = q >> 2, tb = q & 3;
       acc[fb][tb] = mfma(op[slot][fb], op[slot][4 + tb], acc[fb][tb]);
       __builtin_amdgcn_sched_barrier(0);
-      if (q < 8) {
-        if (do_read) read_one(rbuf, rkk, slot ^ 1, q);
-      } else if (q - 8 < nload) {
-        load_one(lstage, lbuf, j0 + q - 8);
-      }
+      if (q < 8 && do_read) read_one(rbuf, rkk, slot ^ 1, q);
+      if ((q & 1) && (q >> 1) < nload) load_one(lstage, lbuf, j0 + (q >> 1));
       __builtin_amdgcn_sched_barrier(0);
     }
   };
