@@ -96,8 +96,8 @@ def cpu_baseline(name, q, k, v, segs, budget_s):
         rows_done += len(rows)
     flops = 4.0 * rows_done * n * W.HEAD_DIM
     return {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": "%s workload, head 0 of 42, query rows 0..%d against all %d keys (RoPE included), "
-                      "%.1f s of fp64 numpy; FLOP 4*rows*N*D" % (name, rows_done - 1, n, t_used)}
+            "sample": "%s workload, head 0 of %d, query rows 0..%d against all %d keys (RoPE included), "
+                      "%.1f s of fp64 numpy; FLOP 4*rows*N*D" % (name, q.shape[1], rows_done - 1, n, t_used)}
 
 
 ADALN_METRIC = "AdaLN gated residual + modulated layer norm GB/s & % HBM peak, 28,192 rows x 5,376"
@@ -359,6 +359,8 @@ def main():
     ap.add_argument("--mode", default="fused", choices=["fused", "prerotated"])
     ap.add_argument("--reuse-refs", action="store_true",
                     help="keep the reference rows' rotated K cached across steps; rotate only text and target rows")
+    ap.add_argument("--heads", type=int, default=0,
+                    help="attention path: number of heads instead of the workload's 42 (a head shard, e.g. 11)")
     ap.add_argument("--no-split", action="store_true",
                     help="attention without a workspace: the last, partly filled wave is not split along the keys")
     ap.add_argument("--path", default="attention", choices=["attention", "adaln", "pack", "qkv"],
@@ -395,6 +397,8 @@ def main():
     h3.load_library()
     dev = torch.device("cuda:0")
     h, segs = W.CONFIGS[args.config]
+    if args.heads:
+        h = args.heads          # one GPU's share of the heads under head (Ulysses) sharding
     n = W.n_tokens(segs)
     D = W.HEAD_DIM
     q, k, v = W.qkv(n, h, W.DEFAULT_SEED)
@@ -469,7 +473,9 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": WORKLOAD if args.config == "5s" else args.config, "n_tokens": n, "heads": h,
+        "config": {"workload": (WORKLOAD if args.config == "5s" and not args.heads else
+                                "%s, %d heads (one GPU's head share)" % (args.config, h) if args.heads else args.config),
+                   "n_tokens": n, "heads": h,
                    "head_dim": D, "rope_sections": list(W.ROPE_SECTIONS), "mode": args.mode,
                    "frac_of_peak_step": round(value / PEAK_BF16_TFLOPS, 4),
                    "tokens_per_s": round(n / (ms_step * 1e-3), 1),

@@ -105,3 +105,21 @@ def test_split_tail_full_size(gpu_lib):
     check(o_ws, lse_ws, q, k, v, segs, [41], np.unique(np.r_[n - 1, 20000, rng.integers(14592, n, 40)]), "5s split")
     check(o_ws, lse_ws, q, k, v, segs, [0], np.unique(np.r_[0, rng.integers(0, n, 30)]), "5s full")
     assert np.all(np.isfinite(lse_ws))
+
+
+@pytest.mark.parametrize("heads", [10, 11])
+def test_head_shard_full_length(gpu_lib, heads):
+    """One GPU's share of the 42 heads under head sharding (11/11/10/10) at the 5 s length, through
+    the benchmark's call; at 10 heads the last wave is split, at 11 it is not."""
+    h3 = gpu_lib
+    _, segs = W.CONFIGS["5s"]
+    n = W.n_tokens(segs)
+    q, k, v = W.qkv(n, heads, seed=40 + heads)
+    need = h3.forward_workspace_bytes(n, heads)
+    print("%d heads: workspace bytes %d" % (heads, need), flush=True)
+    o_ws, lse_ws = run(h3, segs, q, k, v, need)
+    rng = np.random.default_rng(heads)
+    rows = np.unique(np.r_[0, n - 1, rng.integers(0, n, 24)])
+    check(o_ws, lse_ws, q, k, v, segs, [heads - 1], rows, "%d heads, last" % heads)
+    check(o_ws, lse_ws, q, k, v, segs, [0], rows, "%d heads, first" % heads)
+    assert np.all(np.isfinite(lse_ws))
