@@ -205,19 +205,31 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs a) {
   if (s + 1 < nst) stage(s++, True{}, False{});
   stage(s, False{}, False{});
 
-  // epilogue: bias, rotation of whole-head slabs, one rounding to bf16
+  // epilogue: bias, rotation of whole-head slabs, one rounding to bf16.  Everything it reads from
+  // memory is requested up front so that the latencies overlap: the lane's 64 bias values (the same
+  // for every token block), its 4 tokens' coordinates, and the rotation table through wave-uniform
+  // indices (scalar loads; the lane's half hf then selects between two candidate pairs).
   const int fw0 = f0 + wf * 128;                       // first feature of this wave: a head boundary
   const bool rotate = fw0 < a.rope_cols;
+  uint2 bw[4][4];
+#pragma unroll
+  for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      bw[fb][g] = a.bias != nullptr ? *reinterpret_cast<const uint2*>(a.bias + fw0 + fb * 32 + 8 * g + 4 * hf)
+                                    : make_uint2(0, 0);
+  float pos[4][3];
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) {
+    const int token = t0 + wt * 128 + tb * 32 + col;
+    const bool load = rotate && token < a.m;
+#pragma unroll
+    for (int ax = 0; ax < 3; ++ax) pos[tb][ax] = load ? a.coords[3 * int64_t(token) + ax] : 0.0f;
+  }
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb) {
     const int token = t0 + wt * 128 + tb * 32 + col;
     const bool valid = token < a.m;
-    float pos0 = 0.0f, pos1 = 0.0f, pos2 = 0.0f;
-    if (rotate && valid) {
-      pos0 = a.coords[3 * int64_t(token) + 0];
-      pos1 = a.coords[3 * int64_t(token) + 1];
-      pos2 = a.coords[3 * int64_t(token) + 2];
-    }
     uint16_t* yrow = a.y + int64_t(valid ? token : 0) * a.y_stride + fw0;
 #pragma unroll
     for (int fb = 0; fb < 4; ++fb) {
@@ -225,20 +237,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = fb * 32 + 8 * g + 4 * hf;       // head-dim index of register 4 g
-        if (a.bias != nullptr) {
-          const uint2 bw = *reinterpret_cast<const uint2*>(a.bias + fw0 + d0);
-          v[4 * g + 0] += __uint_as_float(bw.x << 16);
-          v[4 * g + 1] += __uint_as_float(bw.x & 0xffff0000u);
-          v[4 * g + 2] += __uint_as_float(bw.y << 16);
-          v[4 * g + 3] += __uint_as_float(bw.y & 0xffff0000u);
-        }
+        v[4 * g + 0] += __uint_as_float(bw[fb][g].x << 16);
+        v[4 * g + 1] += __uint_as_float(bw[fb][g].x & 0xffff0000u);
+        v[4 * g + 2] += __uint_as_float(bw[fb][g].y << 16);
+        v[4 * g + 3] += __uint_as_float(bw[fb][g].y & 0xffff0000u);
         if (rotate) {
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
-            const int pair = (d0 >> 1) + h;
-            const int ax = rope_axis(pair, a.tab);
+            const int u = fb * 16 + 4 * g + h;         // pair of this register pair at hf = 0; + 2 at hf = 1
+            const double f_lo = a.tab.freq[u], f_hi = a.tab.freq[u + 2];
+            const int ax_lo = rope_axis(u, a.tab), ax_hi = rope_axis(u + 2, a.tab);
+            const int ax = hf ? ax_hi : ax_lo;
             float cs, sn;
-            rope_cos_sin(ax == 0 ? pos0 : (ax == 1 ? pos1 : pos2), a.tab.freq[pair], cs, sn);
+            rope_cos_sin(ax == 0 ? pos[tb][0] : (ax == 1 ? pos[tb][1] : pos[tb][2]), hf ? f_hi : f_lo, cs, sn);
             const float x = v[4 * g + 2 * h], y = v[4 * g + 2 * h + 1];
             v[4 * g + 2 * h] = __builtin_fmaf(x, cs, -(y * sn));
             v[4 * g + 2 * h + 1] = __builtin_fmaf(x, sn, y * cs);
