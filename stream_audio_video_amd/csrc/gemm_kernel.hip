@@ -47,8 +47,10 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8;
+typedef __attribute__((address_space(3))) f32x2_t lds_f32x2;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
@@ -226,6 +228,37 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int ax = 0; ax < 3; ++ax) pos[tb][ax] = load ? a.coords[3 * int64_t(token) + ax] : 0.0f;
   }
+  // cos / sin of the lane's rotation pair at register slot (fb, g, h) for token block tb
+  auto angle = [&](int tb, int fb, int g, int h, float& cs, float& sn) {
+    const int u = fb * 16 + 4 * g + h;                 // pair of this register pair at hf = 0; + 2 at hf = 1
+    const double f_lo = a.tab.freq[u], f_hi = a.tab.freq[u + 2];
+    const int ax_lo = rope_axis(u, a.tab), ax_hi = rope_axis(u + 2, a.tab);
+    const int ax = hf ? ax_hi : ax_lo;
+    rope_cos_sin(ax == 0 ? pos[tb][0] : (ax == 1 ? pos[tb][1] : pos[tb][2]), hf ? f_hi : f_lo, cs, sn);
+  };
+  // The angles depend on the token and the pair only, so when both halves of the tile are rotated
+  // the two waves of a token half (wf = 0, 1) need the same values: each computes two of the four
+  // token blocks into LDS (free now: every wave has passed the last stage's barrier, after which no
+  // operand is read) and reads the other two.  Layout [wt][tb][slot][lane] of (cos, sin).
+  const bool share = f0 + 2 * 128 <= a.rope_cols;    // uniform over the workgroup
+  lds_f32x2* cs_lds = (lds_f32x2*)(wt == 0 ? (lds_u16*)as : (lds_u16*)bs);
+  if (share) {
+#pragma unroll
+    for (int tbl = 0; tbl < 2; ++tbl) {
+      const int tb = 2 * wf + tbl;
+#pragma unroll
+      for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            float cs, sn;
+            angle(tb, fb, g, h, cs, sn);
+            cs_lds[(tb * 32 + fb * 8 + g * 2 + h) * 64 + lane] = f32x2_t{cs, sn};
+          }
+    }
+    __syncthreads();
+  }
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb) {
     const int token = t0 + wt * 128 + tb * 32 + col;
@@ -244,12 +277,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs a) {
         if (rotate) {
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
-            const int u = fb * 16 + 4 * g + h;         // pair of this register pair at hf = 0; + 2 at hf = 1
-            const double f_lo = a.tab.freq[u], f_hi = a.tab.freq[u + 2];
-            const int ax_lo = rope_axis(u, a.tab), ax_hi = rope_axis(u + 2, a.tab);
-            const int ax = hf ? ax_hi : ax_lo;
             float cs, sn;
-            rope_cos_sin(ax == 0 ? pos[tb][0] : (ax == 1 ? pos[tb][1] : pos[tb][2]), hf ? f_hi : f_lo, cs, sn);
+            if (share) {
+              const f32x2_t c2 = cs_lds[(tb * 32 + fb * 8 + g * 2 + h) * 64 + lane];
+              cs = c2[0];
+              sn = c2[1];
+            } else {
+              angle(tb, fb, g, h, cs, sn);
+            }
             const float x = v[4 * g + 2 * h], y = v[4 * g + 2 * h + 1];
             v[4 * g + 2 * h] = __builtin_fmaf(x, cs, -(y * sn));
             v[4 * g + 2 * h + 1] = __builtin_fmaf(x, sn, y * cs);

@@ -30,15 +30,37 @@ __device__ __forceinline__ int rope_axis(int pair, const RopeTable& tab) {
   return (pair >= tab.b1) + (pair >= tab.b2);
 }
 
-// cos / sin of the angle pos * freq.  The angle is formed and reduced modulo
-// 2 pi in binary64 (the reduction error is k * 2.4e-16 for k turns, far below
-// binary32 resolution at any exact coordinate), then the binary32 sincos of the
-// remainder in [-pi, pi] is taken.
+// cos / sin of the angle pos * freq.  The angle is formed in binary64 and reduced
+// there to quarter turns, ang = q pi/2 + t with integer q and |t| <= pi/4 (the
+// reduction error is about q * 1e-16).  sin t and cos t are their Taylor
+// polynomials to degree 9 and 10, whose truncation error on |t| <= pi/4 is below
+// 2e-9, evaluated in binary32 by Horner's rule; q mod 4 then swaps and negates
+// them.  There is no branch and no large-argument path (|t| is always small),
+// which keeps the code short where many rotations are unrolled.  Error against
+// the binary64 angle: about 6e-8 (the binary32 rounding of t dominates).
 __device__ __forceinline__ void rope_cos_sin(float pos, double freq, float& c, float& s) {
   const double ang = static_cast<double>(pos) * freq;
-  const double turns = __builtin_rint(ang * 0.15915494309189535);       // round(ang / (2 pi))
-  const float r = static_cast<float>(__builtin_fma(-turns, 6.283185307179586, ang));
-  sincosf(r, &s, &c);
+  const double q = __builtin_rint(ang * 0.63661977236758134);             // ang / (pi / 2)
+  const float t = static_cast<float>(__builtin_fma(-q, 1.5707963267948966, ang));
+  const float t2 = t * t;
+  float ps = 1.0f / 362880.0f;                                             // sin: t - t^3/3! + ... + t^9/9!
+  ps = __builtin_fmaf(ps, t2, -1.0f / 5040.0f);
+  ps = __builtin_fmaf(ps, t2, 1.0f / 120.0f);
+  ps = __builtin_fmaf(ps, t2, -1.0f / 6.0f);
+  const float sn = __builtin_fmaf(ps * t2, t, t);
+  float pc = -1.0f / 3628800.0f;                                           // cos: 1 - t^2/2! + ... - t^10/10!
+  pc = __builtin_fmaf(pc, t2, 1.0f / 40320.0f);
+  pc = __builtin_fmaf(pc, t2, -1.0f / 720.0f);
+  pc = __builtin_fmaf(pc, t2, 1.0f / 24.0f);
+  pc = __builtin_fmaf(pc, t2, -0.5f);
+  const float cs = __builtin_fmaf(pc, t2, 1.0f);
+  // cos(t + q pi/2), sin(t + q pi/2) for q mod 4 = 0, 1, 2, 3:
+  // (cs, sn), (-sn, cs), (-cs, -sn), (sn, -cs)
+  const int qi = static_cast<int>(q) & 3;
+  const float c0 = (qi & 1) ? sn : cs;
+  const float s0 = (qi & 1) ? cs : sn;
+  c = ((qi + 1) & 2) ? -c0 : c0;
+  s = (qi & 2) ? -s0 : s0;
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
