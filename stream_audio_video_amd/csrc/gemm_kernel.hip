@@ -47,10 +47,8 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8;
-typedef __attribute__((address_space(3))) f32x2_t lds_f32x2;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
@@ -236,29 +234,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs a) {
     const int ax = hf ? ax_hi : ax_lo;
     rope_cos_sin(ax == 0 ? pos[tb][0] : (ax == 1 ? pos[tb][1] : pos[tb][2]), hf ? f_hi : f_lo, cs, sn);
   };
-  // The angles depend on the token and the pair only, so when both halves of the tile are rotated
-  // the two waves of a token half (wf = 0, 1) need the same values: each computes two of the four
-  // token blocks into LDS (free now: every wave has passed the last stage's barrier, after which no
-  // operand is read) and reads the other two.  Layout [wt][tb][slot][lane] of (cos, sin).
-  const bool share = f0 + 2 * 128 <= a.rope_cols;    // uniform over the workgroup
-  lds_f32x2* cs_lds = (lds_f32x2*)(wt == 0 ? (lds_u16*)as : (lds_u16*)bs);
-  if (share) {
-#pragma unroll
-    for (int tbl = 0; tbl < 2; ++tbl) {
-      const int tb = 2 * wf + tbl;
-#pragma unroll
-      for (int fb = 0; fb < 4; ++fb)
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            float cs, sn;
-            angle(tb, fb, g, h, cs, sn);
-            cs_lds[(tb * 32 + fb * 8 + g * 2 + h) * 64 + lane] = f32x2_t{cs, sn};
-          }
-    }
-    __syncthreads();
-  }
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb) {
     const int token = t0 + wt * 128 + tb * 32 + col;
@@ -278,13 +253,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs a) {
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             float cs, sn;
-            if (share) {
-              const f32x2_t c2 = cs_lds[(tb * 32 + fb * 8 + g * 2 + h) * 64 + lane];
-              cs = c2[0];
-              sn = c2[1];
-            } else {
-              angle(tb, fb, g, h, cs, sn);
-            }
+            angle(tb, fb, g, h, cs, sn);
             const float x = v[4 * g + 2 * h], y = v[4 * g + 2 * h + 1];
             v[4 * g + 2 * h] = __builtin_fmaf(x, cs, -(y * sn));
             v[4 * g + 2 * h + 1] = __builtin_fmaf(x, sn, y * cs);
