@@ -52,22 +52,32 @@ GEMM_SOURCE = os.path.join(CSRC, "gemm_kernel.hip")
 QKV_TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "linear_qkv_5s_hbm_traffic.json")
 
 
+def kernel_digest(source):
+    """sha256 over a kernel's source and the headers it is compiled with."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in (source, os.path.join(CSRC, "launch.hpp"), os.path.join(CSRC, "rope_math.hpp")):
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
 def measured_traffic(record=TRAFFIC_RECORD, source=ATTN_SOURCE, key="attn_fwd_sha256"):
     """HBM bytes per launch from a committed counter record, or None.
 
     The record holds FETCH_SIZE / WRITE_SIZE per dispatch already scaled by the
-    copy-kernel calibration; it is used only while the kernel source still has
-    the hash the counters were taken with.
+    copy-kernel calibration; it is used only while the kernel's sources (its file,
+    launch.hpp and rope_math.hpp) still have the digest the counters were taken with.
     """
-    import hashlib
     try:
         rec = json.load(open(record))
-        digest = hashlib.sha256(open(source, "rb").read()).hexdigest()
+        digest = kernel_digest(source)
     except (OSError, ValueError):
         return None
     if rec.get(key) != digest:
         return None
     return rec.get("bytes_per_launch")
+
+
 METRIC = "MM-RoPE+attention TFLOP/s & % bf16 MFMA peak, 28,192-token packed seq"
 WORKLOAD = ("5 s 704x1280 packed sequence: 512 text + 31 latent frames x 22x40 video + "
             "200 steps x 2 audio = 28,192 tokens; 42 heads x 128; RoPE t/h/w 32/48/48, base 1e4")
