@@ -10,8 +10,9 @@
 // rotated Q in registers for the whole kernel.  Every K or V operand a wave
 // reads from LDS feeds kQB MFMAs (one per query block), which halves the LDS
 // traffic per MFMA at kQB = 2.  The workgroup streams the head's K and V in
-// tiles of kBN keys through LDS, double-buffered with one barrier per tile: the
-// next tile's loads are in flight while the current tile is computed.  The
+// tiles of kBN keys through three LDS buffers with one barrier per tile: the
+// next tile's loads are in flight while the current tile is computed, and the
+// two waves on each SIMD work half a tile apart (see the tile loop).  The
 // loads use a buffer descriptor rebased on every tile, so rows past the end of
 // the sequence read as zero without any per-lane test.
 //
@@ -80,6 +81,7 @@ constexpr int kKTile = kBN * kKStr;          // elements per K buffer
 constexpr int kVTile = kBN * kVStr;          // elements per V buffer
 constexpr int kChunks = kBN * 16 / kThreads; // 16-byte chunks per thread per tensor per tile
 constexpr int kRowsPerPass = kThreads / 16;  // rows covered by one pass of all threads
+constexpr int kNBuf = 3;                     // K/V tile buffers
 constexpr float kMaxTileSum = 256.0f;        // a lane's tile sum of P above 2^8 raises the reference
 constexpr int kRsrcFlags = 0x00020000;       // raw buffer, 32-bit data format
 static_assert(kBN % 32 == 0 && kChunks >= 1 && kBN * 16 == kChunks * kThreads, "tile shape");
@@ -107,8 +109,8 @@ __device__ __forceinline__ float pair_sum(float x) {
 }
 
 __global__ __launch_bounds__(kThreads, kQB == 1 ? 2 : 1) void attn_fwd_kernel(FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t ks[2 * kKTile];
-  __shared__ __attribute__((aligned(16))) uint16_t vs[2 * kVTile];
+  __shared__ __attribute__((aligned(16))) uint16_t ks[kNBuf * kKTile];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[kNBuf * kVTile];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -316,9 +318,9 @@ __global__ __launch_bounds__(kThreads, kQB == 1 ? 2 : 1) void attn_fwd_kernel(Fw
 
   // One tile: scores, softmax, PV.  The first tile sets the reference max (O and
   // l are still zero); the last one masks keys >= n.
-  auto step = [&](int t, auto first, auto last) {
+  auto softmax_step = [&](int t, auto first, auto last, bf16x8_t (&pb)[kQB][kKB][2]) {
     f32x16_t s[kQB][kKB];
-    scores(t & 1, s);
+    scores(t % kNBuf, s);
     if constexpr (decltype(last)::value) mask_tail(s, t * kBN);
     if constexpr (decltype(first)::value) {
 #pragma unroll
@@ -330,7 +332,6 @@ __global__ __launch_bounds__(kThreads, kQB == 1 ? 2 : 1) void attn_fwd_kernel(Fw
         m_ref[i] = mt;
       }
     }
-    bf16x8_t pb[kQB][kKB][2];
     float lt[kQB];
 #pragma unroll
     for (int i = 0; i < kQB; ++i) lt[i] = probs(s[i], pb[i]);
@@ -357,29 +358,66 @@ __global__ __launch_bounds__(kThreads, kQB == 1 ? 2 : 1) void attn_fwd_kernel(Fw
     }
 #pragma unroll
     for (int i = 0; i < kQB; ++i) l_part[i] += lt[i];
-    pv(t & 1, pb);
+  };
+  auto step = [&](int t, auto first, auto last) {
+    bf16x8_t pb[kQB][kKB][2];
+    softmax_step(t, first, last, pb);
+    pv(t % kNBuf, pb);
   };
 
-  // Double-buffered tiles over [t_begin, t_end), one barrier per tile: tile t+1 is loaded into
-  // registers while tile t is computed, then stored into the other buffer (tile t uses buffer
-  // t & 1).  The last step masks keys >= n, which only bites on the sequence's last tile.
+
+  // Tiles over [t_begin, t_end) in three LDS buffers (tile t in buffer t % 3), one barrier per
+  // tile.  Each wave loads its share of tile t + 1 into registers and stores it between the
+  // barriers that open tiles t and t + 1.  The two waves that share a SIMD are kept half a tile
+  // apart, so that one's softmax runs under the other's MFMAs instead of both competing for the
+  // matrix pipe and then both leaving it idle: the leading half (waves 0 .. kWaves/2 - 1) runs
+  // scores, softmax and PV of tile t after barrier t; the lagging half runs PV of tile t - 1 and
+  // then scores and softmax of tile t, keeping P in registers across the barrier.  The lagging
+  // half still reads V of tile t - 1 after barrier t, hence the third buffer.  Each wave's own
+  // arithmetic is the same in both halves, so the result does not depend on the half.  The last
+  // step masks keys >= n, which only bites on the sequence's last tile.
   load_tile(t_begin);
-  store_tile(t_begin & 1);
+  store_tile(t_begin % kNBuf);
   __syncthreads();
-  if (t_end - t_begin == 1) {
-    step(t_begin, True{}, True{});
-  } else {
-    load_tile(t_begin + 1);
-    step(t_begin, True{}, False{});
-    store_tile((t_begin + 1) & 1);
-    for (int t = t_begin + 1; t + 1 < t_end; ++t) {
+  // waves w and w + kWaves / 2 share a SIMD; the second half runs half a tile behind
+  const bool lag = wave >= kWaves / 2;
+  if (!lag) {
+    if (t_end - t_begin == 1) {
+      step(t_begin, True{}, True{});
+    } else {
+      load_tile(t_begin + 1);
+      step(t_begin, True{}, False{});
+      store_tile((t_begin + 1) % kNBuf);
+      for (int t = t_begin + 1; t + 1 < t_end; ++t) {
+        __syncthreads();
+        load_tile(t + 1);
+        step(t, False{}, False{});
+        store_tile((t + 1) % kNBuf);
+      }
       __syncthreads();
-      load_tile(t + 1);
-      step(t, False{}, False{});
-      store_tile((t + 1) & 1);
+      step(t_end - 1, False{}, True{});
     }
-    __syncthreads();
-    step(t_end - 1, False{}, True{});
+  } else {
+    bf16x8_t pb[kQB][kKB][2];
+    if (t_end - t_begin == 1) {
+      softmax_step(t_begin, True{}, True{}, pb);
+      pv(t_begin % kNBuf, pb);
+    } else {
+      load_tile(t_begin + 1);
+      softmax_step(t_begin, True{}, False{}, pb);
+      store_tile((t_begin + 1) % kNBuf);
+      for (int t = t_begin + 1; t + 1 < t_end; ++t) {
+        __syncthreads();
+        load_tile(t + 1);
+        pv((t - 1) % kNBuf, pb);
+        softmax_step(t, False{}, False{}, pb);
+        store_tile((t + 1) % kNBuf);
+      }
+      __syncthreads();
+      pv((t_end - 2) % kNBuf, pb);
+      softmax_step(t_end - 1, False{}, True{}, pb);
+      pv((t_end - 1) % kNBuf, pb);
+    }
   }
 
   if (part >= 0) {
