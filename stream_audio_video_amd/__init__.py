@@ -235,10 +235,12 @@ def forward_workspace_bytes(n_tokens, n_heads):
 
 
 def mmrope_attention(q, k, v, coords_dev, cfg=None, scale=0.0, want_lse=True, fuse_q=True, k_rot=None,
-                     out=None, lse=None):
+                     out=None, lse=None, split=True):
     """Convenience: rotate K (and Q unless fused), then attend.  q, k, v: bf16 [N, H, 128] CUDA tensors.
 
-    Allocates K~ (and Q~ when not fused), O and LSE with torch unless given.  Returns (O, LSE or None).
+    Allocates K~ (and Q~ when not fused), O, LSE and, with split=True, the workspace that lets the
+    last, partly filled wave of workgroups run split along the keys (h3attn_forward_ws) with torch
+    unless given.  Returns (O, LSE or None).
     """
     import torch
     cfg = cfg or rope_cfg()
@@ -255,6 +257,12 @@ def mmrope_attention(q, k, v, coords_dev, cfg=None, scale=0.0, want_lse=True, fu
     o = torch.empty((n, h, d), dtype=torch.bfloat16, device=q.device) if out is None else out
     if want_lse and lse is None:
         lse = torch.empty((h, n), dtype=torch.float32, device=q.device)
-    forward(cfg, coords_dev, 1 if fuse_q else 0, q_use, k_rot, v, o, lse if want_lse else None, n, h,
-            stride, o.stride(0), scale)
+    ws_bytes = forward_workspace_bytes(n, h) if split and n > 0 else 0
+    if ws_bytes > 0:
+        ws = torch.empty((ws_bytes + 3) // 4, dtype=torch.float32, device=q.device)
+        forward_ws(cfg, coords_dev, 1 if fuse_q else 0, q_use, k_rot, v, o, lse if want_lse else None, n, h,
+                   stride, o.stride(0), scale, ws, ws_bytes)
+    else:
+        forward(cfg, coords_dev, 1 if fuse_q else 0, q_use, k_rot, v, o, lse if want_lse else None, n, h,
+                stride, o.stride(0), scale)
     return o, (lse if want_lse else None)
