@@ -524,20 +524,34 @@ void attn_fwd_schedule(int32_t n, int32_t heads, int32_t cus, int32_t* n_full, i
   *split = 1;
   *tiles_per_split = ntiles;
   *ws_bytes = 0;
-  // only a last wave of workgroups filled to at most half is worth splitting (one workgroup per CU)
+  // One workgroup per CU: the last wave holds rem = units mod cus units and the other CUs idle
+  // for the rest of it.  Cutting those units into s key ranges of tps tiles makes the last
+  // stretch ceil(rem s / cus) waves of tps / ntiles of a unit each, plus the merge, which reads
+  // and writes the partials (about rem s 133 KB at ~4 TB/s, against ~1.75 us per key tile of a
+  // unit).  Take the s in 2 .. 8 (parts of at least 4 tiles) that minimises that, and split only
+  // if it saves at least a tenth of a unit.
   const int rem = cus > 0 ? units % cus : 0;
-  if (units < cus || rem == 0 || 2 * rem > cus || ntiles < 8) return;
-  int s = cus / rem;
-  s = s < 2 ? 2 : (s > 8 ? 8 : s);
-  if (s > ntiles / 4) s = ntiles / 4;
-  if (s < 2) return;
-  const int tps = (ntiles + s - 1) / s;
-  s = (ntiles + tps - 1) / tps;                       // every part non-empty
-  if (s < 2) return;
+  if (units < cus || rem == 0 || ntiles < 8) return;
+  const double part_bytes = double(kBM) * (kHeadDim + 2) * 4;
+  double best = 0.9;
+  int best_s = 1, best_tps = ntiles;
+  for (int s = 2; s <= 8 && 4 * s <= ntiles; ++s) {
+    const int tps = (ntiles + s - 1) / s;
+    const int parts = (ntiles + tps - 1) / tps;        // every part non-empty
+    const int waves = (rem * parts + cus - 1) / cus;
+    const double merge = double(rem) * parts * part_bytes / 4.0e12 / (ntiles * 1.75e-6);
+    const double t = double(waves) * tps / ntiles + merge;
+    if (t < best - 1e-9) {
+      best = t;
+      best_s = parts;
+      best_tps = tps;
+    }
+  }
+  if (best_s < 2) return;
   *n_full = units - rem;
-  *split = s;
-  *tiles_per_split = tps;
-  *ws_bytes = int64_t(rem) * s * kBM * (kHeadDim + 2) * 4;
+  *split = best_s;
+  *tiles_per_split = best_tps;
+  *ws_bytes = int64_t(rem) * best_s * kBM * (kHeadDim + 2) * 4;
 }
 
 }  // namespace h3
