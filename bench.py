@@ -27,6 +27,13 @@ latent [2][200][32]; bytes counted per value: 4 + 4 (state) + 2 (velocity) +
 embedding of Q and K in its epilogue (28,192 x 5,376 -> 3 x 42 x 128, bias,
 synthetic weights), FLOP 2 M N K; the output projection (5,376 -> 5,376, no
 rotation) is timed beside it.
+
+--path block times the attention half of one DiT block over the 5 s rows, five
+calls in a row with bf16 between them: AdaLN modulation, the fused QKV
+projection with Q/K rotation, attention on the projection's strided Q/K/V
+(rope_q = 0, split tail), the output projection, and the gated residual fused
+with the next modulated norm.  FLOP counted: 4 N^2 H D + 2 N C 3C + 2 N C C; the
+roofline object is the attention call's.
 """
 import argparse
 import json
@@ -360,6 +367,118 @@ def bench_qkv(args):
     print(json.dumps(rec), flush=True)
 
 
+BLOCK_METRIC = ("Attention half of a DiT block (AdaLN, fused QKV + RoPE, attention, output projection, "
+                "gated residual + AdaLN) TFLOP/s, 28,192-token packed seq")
+
+
+def block_cpu_baseline(config, x, table, t_idx, tags, w_qkv, b_qkv, coords, segs, flops, adaln_b, budget_s):
+    """Seconds of the fp64 oracle per block, composed from bounded samples of each stage kind."""
+    heads = W.CONFIGS[config][0]
+    n = x.shape[0]
+    q, k, v = W.qkv(n, heads, W.DEFAULT_SEED)
+    att = cpu_baseline(config, q, k, v, segs, budget_s / 3)
+    gem = qkv_cpu_baseline(x, w_qkv, b_qkv, coords, budget_s / 3)
+    ada = adaln_cpu_baseline(x, x, table, t_idx, tags, budget_s / 3)
+    secs = (flops["attention"] / (att["value"] * 1e12) + (flops["qkv"] + flops["out_proj"]) / (gem["value"] * 1e12)
+            + adaln_b / (ada["value"] * 1e9))
+    return {"value": sum(flops.values()) / secs / 1e12, "unit": "TFLOP/s", "cores": max(att["cores"], gem["cores"]),
+            "kind": "oracle",
+            "sample": "per-stage oracle rates applied to the whole block's FLOP and bytes (AdaLN modulate "
+                      "priced at the residual row's byte rate): attention %s; projections %s; AdaLN %s"
+                      % (att["sample"], gem["sample"], ada["sample"])}
+
+
+def bench_block(args):
+    import torch
+    import stream_audio_video_amd as h3
+    h3.load_library()
+    dev = torch.device("cuda:0")
+    heads, segs = W.CONFIGS[args.config]
+    n = W.n_tokens(segs)
+    c = heads * W.HEAD_DIM
+    x, _, table = W.adaln_inputs(n, c)
+    t_idx, tags = W.adaln_rows(segs)
+    _, w_qkv, b_qkv = W.projection_inputs(1, c, 3 * c)
+    _, w_o, b_o = W.projection_inputs(1, c, c, W.DEFAULT_SEED + 1)
+    coords_h = h3.build_coords(segs)
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    xd, tab, wq, bq, wo, bo = to(x), to(table), to(w_qkv), to(b_qkv), to(w_o), to(b_o)
+    ti, tg = torch.from_numpy(t_idx).to(dev), torch.from_numpy(tags).to(dev)
+    coords = torch.from_numpy(coords_h).to(dev)
+    cfg = h3.rope_cfg()
+    base = tab.data_ptr()                    # planes [E][6][C]: shift_a, scale_a, gate_a, shift_m, scale_m, gate_m
+    n_e = table.shape[0]
+    h1 = torch.empty_like(xd)
+    qkv = torch.empty((n, 3, heads, W.HEAD_DIM), dtype=torch.bfloat16, device=dev)
+    o = torch.empty((n, heads, W.HEAD_DIM), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((heads, n), dtype=torch.float32, device=dev)
+    ws_bytes = h3.forward_workspace_bytes(n, heads)
+    ws = torch.empty(max(ws_bytes, 16) // 4, dtype=torch.float32, device=dev)
+    y = torch.empty_like(xd)
+    x_out, h2 = torch.empty_like(xd), torch.empty_like(xd)
+    stages = ["adaln_modulate", "qkv_rope", "attention", "out_proj", "adaln_residual"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        h3.adaln_modulate(xd, c, ti, tg, base, base + 2 * c, 6 * c, n_e, h1, c, n, c, h3.LAYER_NORM, 1e-6)
+        mark(1)
+        h3.linear(h1, c, wq, c, bq, qkv, 3 * c, n, 3 * c, c, cfg, coords, 2 * c)
+        mark(2)
+        h3.forward_ws(cfg, coords, 0, qkv[:, 0], qkv[:, 1], qkv[:, 2], o, lse, n, heads, 3 * c, c, 0.0, ws, ws_bytes)
+        mark(3)
+        h3.linear(o, c, wo, c, bo, y, c, n, c, c)
+        mark(4)
+        h3.adaln_residual(xd, y, c, ti, tg, base + 4 * c, base + 6 * c, base + 8 * c, 6 * c, n_e, x_out, h2, c, n,
+                          c, h3.LAYER_NORM, 1e-6)
+        mark(5)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    stage_ms = {s: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, s in enumerate(stages)}
+    flops = {"attention": 4.0 * n * n * heads * W.HEAD_DIM, "qkv": 2.0 * n * c * 3 * c, "out_proj": 2.0 * n * c * c}
+    total = sum(flops.values())
+    value = total / (ms_step * 1e-3) / 1e12
+    achieved = flops["attention"] / (stage_ms["attention"] * 1e-3) / 1e12
+    mod_b = 2 * n * c * 2 + 8 * n + 2 * n_e * c * 2          # modulate: x read, h written, selectors, 2 planes
+    res_b = adaln_bytes(n, c, n_e)
+    adaln_b = mod_b + res_b
+    cpu = None
+    if args.cpu_budget > 0:
+        cpu = block_cpu_baseline(args.config, x, table, t_idx, tags, w_qkv, b_qkv, coords_h, segs, flops, adaln_b,
+                                 args.cpu_budget)
+    rec = {
+        "metric": BLOCK_METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": WORKLOAD if args.config == "5s" else args.config, "n_tokens": n, "heads": heads,
+                   "hidden": c, "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+                   "stage_TFLOPs": {"qkv_rope": round(flops["qkv"] / (stage_ms["qkv_rope"] * 1e-3) / 1e12, 2),
+                                    "attention": round(achieved, 2),
+                                    "out_proj": round(flops["out_proj"] / (stage_ms["out_proj"] * 1e-3) / 1e12, 2)},
+                   "stage_GBps": {"adaln_modulate": round(mod_b / (stage_ms["adaln_modulate"] * 1e-3) / 1e9, 1),
+                                  "adaln_residual": round(res_b / (stage_ms["adaln_residual"] * 1e-3) / 1e9, 1)},
+                   "tokens_per_s": round(n / (ms_step * 1e-3), 1), "workspace_bytes": ws_bytes,
+                   "flop_per_step": total},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},   # Q arrives rotated here (rope_q = 0): no counter record for this launch
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -373,7 +492,7 @@ def main():
                     help="attention path: number of heads instead of the workload's 42 (a head shard, e.g. 11)")
     ap.add_argument("--no-split", action="store_true",
                     help="attention without a workspace: the last, partly filled wave is not split along the keys")
-    ap.add_argument("--path", default="attention", choices=["attention", "adaln", "pack", "qkv"],
+    ap.add_argument("--path", default="attention", choices=["attention", "adaln", "pack", "qkv", "block"],
                     help="attention: MM-RoPE + attention (the headline); adaln: the AdaLN residual row")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing (0 = skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -400,6 +519,9 @@ def main():
         return
     if args.path == "qkv":
         bench_qkv(args)
+        return
+    if args.path == "block":
+        bench_block(args)
         return
 
     import torch
@@ -493,7 +615,10 @@ def main():
                    "attn_ms": round(attn_ms, 4), "rope_rows": rope_rows,
                    "reuse_refs": bool(args.reuse_refs), "workspace_bytes": ws_bytes},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic()},
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     # the counter record covers the default launch only: 5 s, 42 heads, Q rotated in the kernel
+                     "traffic": (measured_traffic() if args.config == "5s" and not args.heads and not args.no_split
+                                 and fused else None)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
