@@ -283,23 +283,36 @@ __global__ __launch_bounds__(kThreads, kQB == 1 ? 2 : 1) void attn_fwd_kernel(Fw
     return pair_max(mt);
   };
 
-  // O^T += V^T P^T over the tile's 16-key chunks and four 32-dim blocks of V buffer `buf`
-  auto pv = [&](int buf, const bf16x8_t (&pb)[kQB][kKB][2]) {
-    const lds_u16* vt = vsl + buf * kVTile + v_rd;
+  // V^T operand of 16-key chunk kc and 32-dim block db of V buffer `buf`
+  auto vread = [&](int buf, int kc, int db) {
+    const lds_u16* vt = vsl + buf * kVTile + v_rd + (16 * kc) * kVStr + 32 * db;
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_i16x4*>(const_cast<lds_u16*>(vt)));
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<lds_i16x4*>(const_cast<lds_u16*>(vt + 8 * kVStr)));
+    const i16x4_t both[2] = {lo, hi};
+    return __builtin_bit_cast(bf16x8_t, both);
+  };
+  // O^T += V^T P^T over the tile's 16-key chunks and four 32-dim blocks of V buffer `buf`; the
+  // operands of the first kVPre chunks may have been read already (pre)
+  constexpr int kVPre = 2;
+  auto pv_pre = [&](int buf, const bf16x8_t (&pb)[kQB][kKB][2], const bf16x8_t (&pre)[kVPre][4], auto use_pre) {
 #pragma unroll
-    for (int kc = 0; kc < 2 * kKB; ++kc) {
+    for (int kc = 0; kc < 2 * kKB; ++kc)
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            reinterpret_cast<lds_i16x4*>(const_cast<lds_u16*>(vt + (16 * kc) * kVStr + 32 * db)));
-        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            reinterpret_cast<lds_i16x4*>(const_cast<lds_u16*>(vt + (16 * kc + 8) * kVStr + 32 * db)));
-        const i16x4_t both[2] = {lo, hi};
-        const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, both);
+        bf16x8_t vop;
+        if constexpr (decltype(use_pre)::value) {
+          vop = kc < kVPre ? pre[kc < kVPre ? kc : 0][db] : vread(buf, kc, db);
+        } else {
+          vop = vread(buf, kc, db);
+        }
 #pragma unroll
         for (int i = 0; i < kQB; ++i) oacc[i][db] = mfma32(vop, pb[i][kc >> 1][kc & 1], oacc[i][db]);
       }
-    }
+  };
+  auto pv = [&](int buf, const bf16x8_t (&pb)[kQB][kKB][2]) {
+    bf16x8_t none[kVPre][4];
+    pv_pre(buf, pb, none, False{});
   };
 
   // keys past the end of the sequence take no weight (last tile only)
@@ -373,7 +386,8 @@ __global__ __launch_bounds__(kThreads, kQB == 1 ? 2 : 1) void attn_fwd_kernel(Fw
   // matrix pipe and then both leaving it idle: the leading half (waves 0 .. kWaves/2 - 1) runs
   // scores, softmax and PV of tile t after barrier t; the lagging half runs PV of tile t - 1 and
   // then scores and softmax of tile t, keeping P in registers across the barrier.  The lagging
-  // half still reads V of tile t - 1 after barrier t, hence the third buffer.  Each wave's own
+  // half still reads V of tile t - 1 after barrier t, hence the third buffer; it reads the first
+  // of those operands while it waits at the barrier.  Each wave's own
   // arithmetic is the same in both halves, so the result does not depend on the half.  The last
   // step masks keys >= n, which only bites on the sequence's last tile.
   load_tile(t_begin);
@@ -407,9 +421,19 @@ __global__ __launch_bounds__(kThreads, kQB == 1 ? 2 : 1) void attn_fwd_kernel(Fw
       softmax_step(t_begin, True{}, False{}, pb);
       store_tile((t_begin + 1) % kNBuf);
       for (int t = t_begin + 1; t + 1 < t_end; ++t) {
-        __syncthreads();
+        // V of tile t - 1 has been visible since barrier t - 1.  Barrier t is taken in two
+        // halves (release, then wait and acquire) so that the first PV operands are read while
+        // this wave waits for the others.
+        bf16x8_t pre[kVPre][4];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+#pragma unroll
+        for (int kc = 0; kc < kVPre; ++kc)
+#pragma unroll
+          for (int db = 0; db < 4; ++db) pre[kc][db] = vread((t - 1) % kNBuf, kc, db);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
         load_tile(t + 1);
-        pv((t - 1) % kNBuf, pb);
+        pv_pre((t - 1) % kNBuf, pb, pre, True{});
         softmax_step(t, False{}, False{}, pb);
         store_tile((t + 1) % kNBuf);
       }
