@@ -225,7 +225,7 @@ int h3attn_adaln_residual(const void* x, const void* y, int64_t xy_stride, const
  *   rope_cols  0 <= rope_cols <= n_out, multiple of 128
  * Strides are in elements, multiples of 8 (x, w >= k; y >= n_out); pointers
  * 16-byte aligned.  Arithmetic: float32 accumulation of exact bf16 products.
- * m == 0 is a no-op.  Errors: EINVAL, ERANGE (m >= 2^31, 256 rows of x or w
+ * m == 0 is a no-op.  Errors: EINVAL, ERANGE (m >= 2^31, 256 rows of x, w or y
  * spanning 2^31 bytes, x spanning 2^32 bytes), EUNSUPPORTED, EHIP.
  */
 #define H3ATTN_LINEAR_TILE 256

@@ -47,6 +47,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8;
 
@@ -208,7 +209,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs a) {
   // epilogue: bias, rotation of whole-head slabs, one rounding to bf16.  Everything it reads from
   // memory is requested up front so that the latencies overlap: the lane's 64 bias values (the same
   // for every token block), its 4 tokens' coordinates, and the rotation table through wave-uniform
-  // indices (scalar loads; the lane's half hf then selects between two candidate pairs).
+  // indices (scalar loads; the lane's half hf then selects between two candidate pairs).  Nothing
+  // is hoisted across token blocks: more live state here makes the allocator spill accumulators.
   const int fw0 = f0 + wf * 128;                       // first feature of this wave: a head boundary
   const bool rotate = fw0 < a.rope_cols;
   uint2 bw[4][4];
@@ -218,27 +220,37 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs a) {
     for (int g = 0; g < 4; ++g)
       bw[fb][g] = a.bias != nullptr ? *reinterpret_cast<const uint2*>(a.bias + fw0 + fb * 32 + 8 * g + 4 * hf)
                                     : make_uint2(0, 0);
+  // the lane's 4 tokens' coordinates through a descriptor over this wave's token rows (rows past
+  // m read as zero), and the output through one over the same rows (their stores are dropped)
+  const int tw0 = t0 + wt * 128;
+  const int rows = min(a.m - tw0, 128);                // may be <= 0 on the last token tile
+  const int yrow_bytes = static_cast<int>(a.y_stride * 2);
   float pos[4][3];
+  if (rotate) {
+    const __amdgpu_buffer_rsrc_t cd = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(a.coords) + 3 * int64_t(tw0), 0, rows > 0 ? rows * 12 : 0, kRsrcFlags);
 #pragma unroll
-  for (int tb = 0; tb < 4; ++tb) {
-    const int token = t0 + wt * 128 + tb * 32 + col;
-    const bool load = rotate && token < a.m;
+    for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-    for (int ax = 0; ax < 3; ++ax) pos[tb][ax] = load ? a.coords[3 * int64_t(token) + ax] : 0.0f;
+      for (int ax = 0; ax < 3; ++ax)
+        pos[tb][ax] =
+            __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(cd, (tb * 32 + col) * 12 + 4 * ax, 0, 0));
   }
+  const __amdgpu_buffer_rsrc_t yd = __builtin_amdgcn_make_buffer_rsrc(
+      a.y + int64_t(tw0) * a.y_stride + fw0, 0, rows > 0 ? (rows - 1) * yrow_bytes + 256 : 0, kRsrcFlags);
   // cos / sin of the lane's rotation pair at register slot (fb, g, h) for token block tb
   auto angle = [&](int tb, int fb, int g, int h, float& cs, float& sn) {
     const int u = fb * 16 + 4 * g + h;                 // pair of this register pair at hf = 0; + 2 at hf = 1
     const double f_lo = a.tab.freq[u], f_hi = a.tab.freq[u + 2];
     const int ax_lo = rope_axis(u, a.tab), ax_hi = rope_axis(u + 2, a.tab);
     const int ax = hf ? ax_hi : ax_lo;
-    rope_cos_sin(ax == 0 ? pos[tb][0] : (ax == 1 ? pos[tb][1] : pos[tb][2]), hf ? f_hi : f_lo, cs, sn);
+    float p = ax == 1 ? pos[tb][1] : pos[tb][2];       // two selects, not a branch
+    p = ax == 0 ? pos[tb][0] : p;
+    rope_cos_sin(p, hf ? f_hi : f_lo, cs, sn);
   };
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb) {
-    const int token = t0 + wt * 128 + tb * 32 + col;
-    const bool valid = token < a.m;
-    uint16_t* yrow = a.y + int64_t(valid ? token : 0) * a.y_stride + fw0;
+    const int yrow = (tb * 32 + col) * yrow_bytes;
 #pragma unroll
     for (int fb = 0; fb < 4; ++fb) {
       f32x16_t v = acc[fb][tb];
@@ -259,9 +271,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs a) {
             v[4 * g + 2 * h + 1] = __builtin_fmaf(x, sn, y * cs);
           }
         }
-        if (valid)
-          *reinterpret_cast<uint2*>(yrow + d0) = make_uint2(pack_bf16x2(v[4 * g + 0], v[4 * g + 1]),
-                                                            pack_bf16x2(v[4 * g + 2], v[4 * g + 3]));
+        const uint2 w = make_uint2(pack_bf16x2(v[4 * g + 0], v[4 * g + 1]), pack_bf16x2(v[4 * g + 2], v[4 * g + 3]));
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, w), yd, yrow + d0 * 2, 0, 0);
       }
     }
   }

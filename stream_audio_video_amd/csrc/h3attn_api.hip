@@ -390,7 +390,8 @@ extern "C" int h3attn_linear(const void* x, int64_t x_stride, const void* w, int
   }
   // byte offsets inside a 256-row tile and over x are 32-bit
   if (m >= (int64_t(1) << 31) || int64_t(H3ATTN_LINEAR_TILE) * x_stride * 2 >= (int64_t(1) << 31) ||
-      int64_t(H3ATTN_LINEAR_TILE) * w_stride * 2 >= (int64_t(1) << 31) || m * x_stride * 2 >= (int64_t(1) << 32))
+      int64_t(H3ATTN_LINEAR_TILE) * w_stride * 2 >= (int64_t(1) << 31) ||
+      int64_t(H3ATTN_LINEAR_TILE) * y_stride * 2 >= (int64_t(1) << 31) || m * x_stride * 2 >= (int64_t(1) << 32))
     return H3ATTN_ERANGE;
   if (m == 0) return H3ATTN_OK;
   const int64_t yb = span_bytes(m, y_stride, n_out);

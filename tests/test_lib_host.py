@@ -240,4 +240,5 @@ def test_abi_rejects_bad_linear_calls(h3):
     assert lin(cf=_cfg(h3, head_dim=64)) == E
     assert lin(y=X + 4096) == E and lin(y=Wt) == E and lin(b=Y + 64) == E   # y overlaps an input
     assert lin(xs=2 ** 22 + 8) == R                          # a 256-row tile of x spans 2^31 bytes
+    assert lin(ys=2 ** 22) == R and lin(ws=2 ** 22) == R      # ... of y, of w
     assert lin(m=2 ** 19, xs=5376) == R                      # x spans 2^32 bytes
