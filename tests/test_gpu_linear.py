@@ -113,6 +113,27 @@ def test_plain_projection_and_strides(gpu_lib):
     assert np.all(y[:, n:] == host_bits(torch.full((1,), 3.0, dtype=torch.bfloat16))[0])   # padding untouched
 
 
+@pytest.mark.parametrize("rope", [False, True])
+def test_rows_past_m_untouched(gpu_lib, rope):
+    """y rows past m (here guard rows of the same allocation) keep their contents: the last token
+    tile is partly filled (m = 300: its second 128-row half holds no row at all)."""
+    m, heads, k = 300, 1, 256
+    n = 3 * heads * 128 + 128
+    x, w, b = W.projection_inputs(m, k, n, seed=41)
+    coords_h = gpu_lib.build_coords(segs_of(m))
+    yd = torch.full((m + 300, n), 3.0, dtype=torch.bfloat16, device="cuda")
+    gpu_lib.linear(dev_bf16(x), k, dev_bf16(w), k, dev_bf16(b), yd, n, m, n, k,
+                   gpu_lib.rope_cfg() if rope else None, torch.from_numpy(coords_h).cuda() if rope else None,
+                   2 * heads * 128 if rope else 0)
+    torch.cuda.synchronize()
+    y = host_bits(yd)
+    assert np.all(y[m:] == host_bits(torch.full((1,), 3.0, dtype=torch.bfloat16))[0])
+    yr = linear(f64(x), f64(w), f64(b))
+    if rope:
+        yr[:, :256] = qkv_rope(f64(x), f64(w[:384]), f64(b[:384]), coords_h, heads, SEC, TH)[:, :256]
+    check(y[:m], yr, f64(x), f64(w), f64(b), 2 * heads * 128 if rope else 0, "guard rows rope=%d" % rope)
+
+
 def test_full_size_qkv_sampled(gpu_lib):
     """The 5 s fused QKV projection (28,192 x 5,376 -> 16,128) in the benchmark's launch shape; sampled rows."""
     _, segs = W.CONFIGS["5s"]
