@@ -60,11 +60,16 @@ QKV_TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "linear_qkv_5s_hbm_traffic.j
 
 
 def kernel_digest(source):
-    """sha256 over a kernel's source and the headers it is compiled with."""
+    """sha256 over a kernel's source and the headers it is compiled with, comments and whitespace
+    removed (a comment edit does not change the kernel the counters describe)."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in (source, os.path.join(CSRC, "launch.hpp"), os.path.join(CSRC, "rope_math.hpp")):
-        h.update(open(f, "rb").read())
+        text = open(f, encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 
@@ -73,7 +78,8 @@ def measured_traffic(record=TRAFFIC_RECORD, source=ATTN_SOURCE, key="attn_fwd_sh
 
     The record holds FETCH_SIZE / WRITE_SIZE per dispatch already scaled by the
     copy-kernel calibration; it is used only while the kernel's sources (its file,
-    launch.hpp and rope_math.hpp) still have the digest the counters were taken with.
+    launch.hpp and rope_math.hpp, comments aside) still have the digest the counters
+    were taken with.
     """
     try:
         rec = json.load(open(record))

@@ -8,8 +8,11 @@
 // Work split.  A workgroup of kWaves waves owns kBM = 32 * kQB * kWaves query
 // rows of one head; each wave owns kQB blocks of 32 query rows and keeps their
 // rotated Q in registers for the whole kernel.  Every K or V operand a wave
-// reads from LDS feeds kQB MFMAs (one per query block), which halves the LDS
-// traffic per MFMA at kQB = 2.  The workgroup streams the head's K and V in
+// reads from LDS feeds kQB MFMAs (one per query block).  The build uses kQB = 1
+// and eight waves (256 rows, two waves per SIMD); kQB = 2 (one wave per SIMD,
+// half the LDS traffic per MFMA) still compiles but runs slower, because a
+// wave's own exponentials then stall its MFMAs and the compiler shuffles the
+// accumulators between register files.  The workgroup streams the head's K and V in
 // tiles of kBN keys through three LDS buffers with one barrier per tile: the
 // next tile's loads are in flight while the current tile is computed, and the
 // two waves on each SIMD work half a tile apart (see the tile loop).  The
