@@ -106,7 +106,11 @@ int h3attn_build_coords(const h3attn_segment* segs, int32_t n_segs, float* coord
 /*
  * Device call.  Rotates Q and/or K by the rows' coordinates (the rope() step of
  * the position chain; V is never rotated).  Out-of-place, or in place when
- * the output pointer equals the input pointer.  The cos/sin of each
+ * the output pointer equals the input pointer.  Apart from that exact in-place
+ * case, an output shares no byte with another output, an input or the
+ * coordinates (EINVAL); views that interleave rows of one buffer without
+ * sharing bytes, such as the Q and K slots of a [N][3][H][128] projection
+ * output, are accepted.  The cos/sin of each
  * (row, pair) angle are formed once per row from a binary64 angle and reused
  * over all heads; the rotation runs in float32 and rounds to bfloat16 (nearest
  * even).
@@ -126,9 +130,12 @@ int h3attn_rope_qk(const h3attn_rope_cfg* cfg, const float* coords_dev,
  * Device call.  Per head, O = softmax(Q~ K^T * scale) V over all n_tokens rows:
  * full bidirectional attention with no mask (section 6 of the thread; the open
  * release runs full attention).  K must already be rotated (h3attn_rope_qk with
- * q = NULL).  Q is rotated inside the kernel's Q-tile load when rope_q != 0
- * (same rounding as h3attn_rope_qk, so both routes give identical bits), or used
- * as given when rope_q == 0 (already rotated).
+ * q = NULL).  Q is rotated inside the kernel's Q-tile load when rope_q != 0,
+ * or used as given when rope_q == 0 (already rotated).  The kernel multiplies
+ * Q~ by scale * log2(e) and rounds it to bf16 for the matrix cores: with
+ * rope_q != 0 the rotation and that scaling run in float32 and round once;
+ * a pre-rotated Q~ (already rounded by h3attn_rope_qk) is rounded once more,
+ * so the fused route is the more accurate of the two.
  *   cfg, coords_dev   as above (coords_dev may be NULL when rope_q == 0)
  *   q, k, v           bf16 [n_tokens][n_heads][128], row stride row_stride_qkv
  *   o                 out: bf16 [n_tokens][n_heads][128], row stride row_stride_o
@@ -277,10 +284,12 @@ int h3attn_audio_euler_pack(float* latent, int32_t n_ch, int32_t steps, int32_t 
  * Device call.  h3attn_forward with a caller-owned scratch workspace (device
  * memory, 16-byte aligned, not overlapping any tensor argument).  The attention
  * runs one workgroup per (head, 256-row query block) on each compute unit in
- * waves; when the last wave would be at most half full, its units are split
- * along the keys over several workgroups that leave float32 partial results
- * (unnormalised O and the row's max / sum) in the workspace, merged by a second
- * kernel with the same max-and-rescale rule.  The result equals h3attn_forward
+ * waves; the units of the last, partly filled wave may be split along the keys
+ * over several workgroups that leave float32 partial results (unnormalised O
+ * and the row's max / sum) in the workspace, merged by a second kernel with the
+ * same max-and-rescale rule.  A cost model of that last stretch (the waves of
+ * parts it takes, plus the merge's traffic) picks the number of parts, 2 to 8,
+ * and splits only when that saves at least a tenth of a unit's time.  The result equals h3attn_forward
  * up to the rounding order of the split rows.  A NULL or too small workspace
  * runs the unsplit schedule (h3attn_forward); the library still allocates
  * nothing.  The workspace must not be shared by calls in flight at once.

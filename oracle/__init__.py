@@ -28,11 +28,11 @@ Modules:
   linear     - the attention projections, with Q and K rotated (fused QKV)
 """
 from .coords import build_coords, f32_round, video_hw_f64
-from .rope import inv_freq, rope
+from .rope import rope
 from .attention import attention, bf16_bits_to_f64
 from . import adaln
 from . import pack
 from . import linear
 
-__all__ = ["build_coords", "f32_round", "video_hw_f64", "inv_freq", "rope",
+__all__ = ["build_coords", "f32_round", "video_hw_f64", "rope",
            "attention", "bf16_bits_to_f64", "adaln", "pack", "linear"]

@@ -16,17 +16,6 @@ All arithmetic is float64; coordinates enter as their float32 values.
 import numpy as np
 
 
-def inv_freq(sections, thetas):
-    """Per-pair (axis, frequency) for a head of sum(sections) dims: two arrays of length D/2."""
-    axes, freqs = [], []
-    for a in range(3):
-        d = int(sections[a])
-        for p in range(d // 2):
-            axes.append(a)
-            freqs.append(float(thetas[a]) ** (-(2.0 * p) / d))
-    return np.array(axes, np.int64), np.array(freqs, np.float64)
-
-
 def rope(x, coords, sections, thetas):
     """Rotate x [N, H, D] (any float dtype) by coords [N, 3]; returns float64 [N, H, D]."""
     x = np.asarray(x, dtype=np.float64)

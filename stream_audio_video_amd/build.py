@@ -52,6 +52,7 @@ def build(verbose=False, save_temps=False, out=None, extra_flags=(), build_dir=N
     bdir = build_dir or BUILD
     src_dir = csrc or CSRC
     os.makedirs(bdir, exist_ok=True)
+    os.makedirs(os.path.dirname(os.path.abspath(out)), exist_ok=True)
     jobs = []
     for src in HIP_SOURCES:
         obj = os.path.join(bdir, src + ".o")

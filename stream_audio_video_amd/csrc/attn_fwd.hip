@@ -31,9 +31,10 @@
 // of the PV product is free, so the keys fed to each PV step are the ones the
 // S^T accumulator layout leaves in that lane.
 //
-// Online softmax in base 2, biased.  Q~ is pre-scaled by scale * log2(e)
-// (after its own bf16 rounding, so both rope routes stay bit-identical), and
-// every score chain starts from an accumulator holding -m, the row's running
+// Online softmax in base 2, biased.  Q~ is pre-scaled by scale * log2(e): with
+// rope_q set, Q is rotated and scaled in binary32 and rounded to bf16 once; a
+// Q~ that arrives rotated (and so already rounded) is rounded again after the
+// scaling.  Every score chain starts from an accumulator holding -m, the row's running
 // reference max in those units: the MFMA itself returns s - m, so P = exp2 of
 // the accumulator with no per-score arithmetic.  The reference is raised only
 // when a tile's probabilities get large: each lane sums its tile's P (v_dot2 on
@@ -145,30 +146,34 @@ __global__ __launch_bounds__(kThreads, kQB == 1 ? 2 : 1) void attn_fwd_kernel(Fw
     qrow[i] = qblk * kBM + (wave * kQB + i) * 32 + col;
     const bool qvalid = qrow[i] < a.n;
     const uint16_t* qp = a.q + (qvalid ? qrow[i] : 0) * a.stride_qkv + head * kHeadDim + 8 * hf;
-    float pos[3] = {0.0f, 0.0f, 0.0f};
+    // the row's (t, h, w), picked per pair by selects (an indexed array would be placed in LDS)
+    float pt = 0.0f, ph = 0.0f, pw = 0.0f;
     if (a.rope_q && qvalid) {
-      pos[0] = a.coords[3 * qrow[i] + 0];
-      pos[1] = a.coords[3 * qrow[i] + 1];
-      pos[2] = a.coords[3 * qrow[i] + 2];
+      pt = a.coords[3 * qrow[i] + 0];
+      ph = a.coords[3 * qrow[i] + 1];
+      pw = a.coords[3 * qrow[i] + 2];
     }
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       uint4 x = make_uint4(0, 0, 0, 0);
       if (qvalid) x = *reinterpret_cast<const uint4*>(qp + 16 * c);
       if (a.rope_q) {
+        // rotation and the pre-scale by scale * log2(e) in binary32, then one bf16 rounding
         uint32_t w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           const int pair = 8 * c + 4 * hf + p;
           float cs, sn;
-          rope_cos_sin(pos[rope_axis(pair, a.tab)], a.tab.freq[pair], cs, sn);
-          w[p] = rope_rotate_word(w[p], cs, sn);
+          const int ax = rope_axis(pair, a.tab);
+          rope_cos_sin(ax == 0 ? pt : (ax == 1 ? ph : pw), a.tab.freq[pair], cs, sn);
+          w[p] = rope_rotate_word(w[p], cs * qscale, sn * qscale);
         }
         x = make_uint4(w[0], w[1], w[2], w[3]);
+      } else {
+        // Q~ arrives rotated and rounded: pre-scale by scale * log2(e), rounding once more
+        x = make_uint4(scale_word(x.x, qscale), scale_word(x.y, qscale), scale_word(x.z, qscale),
+                       scale_word(x.w, qscale));
       }
-      // pre-scale by scale * log2(e), rounding once more to bf16
-      x = make_uint4(scale_word(x.x, qscale), scale_word(x.y, qscale), scale_word(x.z, qscale),
-                     scale_word(x.w, qscale));
       qf[i][c] = __builtin_bit_cast(bf16x8_t, x);
     }
   }

@@ -63,6 +63,23 @@ bool overlaps(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
   return a0 < b0 + uintptr_t(b_bytes) && b0 < a0 + uintptr_t(a_bytes);
 }
 
+// Whether two row views with the same row pitch share a byte: rows r of view x cover
+// [x + r * pitch, x + r * pitch + width) for r < rows, with width <= pitch.  Rows r1 of a and
+// r2 of b meet iff |d - j * pitch| < width for d = b - a and j = r1 - r2 in (-rows, rows); only
+// the two j next to d / pitch can come that close.  Views of one fused buffer that interleave
+// rows without sharing bytes (Q and K slots of a [N][3][H][D] projection output) do not overlap.
+bool views_overlap(const void* a, const void* b, int64_t rows, int64_t pitch, int64_t width) {
+  const int64_t d = static_cast<int64_t>(reinterpret_cast<uintptr_t>(b) - reinterpret_cast<uintptr_t>(a));
+  int64_t j = d / pitch;
+  if (d < 0 && j * pitch != d) --j;   // floor
+  for (int64_t jj = j; jj <= j + 1; ++jj) {
+    if (jj <= -rows || jj >= rows) continue;
+    const int64_t gap = d - jj * pitch;
+    if (gap > -width && gap < width) return true;
+  }
+  return false;
+}
+
 }  // namespace
 
 extern "C" int h3attn_rope_qk(const h3attn_rope_cfg* cfg, const float* coords_dev,
@@ -81,6 +98,23 @@ extern "C" int h3attn_rope_qk(const h3attn_rope_cfg* cfg, const float* coords_de
   if (rc != H3ATTN_OK) return rc;
   if (n_tokens == 0) return H3ATTN_OK;
   if (coords_dev == nullptr) return H3ATTN_EINVAL;
+  // an output may be its own input exactly (in place); it shares no byte with any other tensor
+  {
+    const int64_t pitch = row_stride * 2, width = int64_t(n_heads) * h3::kHeadDim * 2;
+    const int64_t span = (n_tokens - 1) * pitch + width;
+    const void* ins[2] = {q_in, k_in};
+    const void* outs[2] = {q_out, k_out};
+    for (int o = 0; o < 2; ++o) {
+      if (outs[o] == nullptr) continue;
+      if (overlaps(outs[o], span, coords_dev, n_tokens * 12)) return H3ATTN_EINVAL;
+      for (int i = 0; i < 2; ++i)
+        if (ins[i] != nullptr && !(i == o && ins[i] == outs[o]) &&
+            views_overlap(ins[i], outs[o], n_tokens, pitch, width))
+          return H3ATTN_EINVAL;
+      if (o == 1 && outs[0] != nullptr && views_overlap(outs[0], outs[1], n_tokens, pitch, width))
+        return H3ATTN_EINVAL;
+    }
+  }
   rc = check_device();
   if (rc != H3ATTN_OK) return rc;
   a.coords = coords_dev;

@@ -4,7 +4,8 @@ against h3attn_forward (MI355X, gfx950).
 Units that run over all keys are computed exactly as by h3attn_forward (bit-equal);
 split units are merged from key-range partials, which changes only the rounding
 order, so they are held to the attention tolerances of the other parity tests
-(max |err| <= 2e-2, RMS <= 2e-3, |LSE err| <= 1e-2).
+(max |err| <= 2e-2, RMS <= 2e-3, |LSE err| <= tolerances.lse_bound(N), the bound
+derived from the bf16 roundings of Q~, K~ and P).
 """
 import numpy as np
 import pytest
@@ -12,6 +13,7 @@ import torch
 
 import oracle
 import workloads as W
+from tolerances import lse_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -51,7 +53,7 @@ def check(o_bits, lse, q, k, v, segs, heads, rows, tag):
     err = f64(o_bits[rows][:, heads]) - o_ref
     le = np.abs(lse[heads][:, rows] - lse_ref).max()
     print("%s max|err| %.3e rms %.3e lse %.3e" % (tag, np.abs(err).max(), np.sqrt((err ** 2).mean()), le), flush=True)
-    assert np.abs(err).max() <= 2e-2 and np.sqrt((err ** 2).mean()) <= 2e-3 and le <= 1e-2
+    assert np.abs(err).max() <= 2e-2 and np.sqrt((err ** 2).mean()) <= 2e-3 and le <= lse_bound(q.shape[0])
 
 
 def test_split_tail_small(gpu_lib):
@@ -110,7 +112,7 @@ def test_split_tail_full_size(gpu_lib):
 @pytest.mark.parametrize("heads", [10, 11])
 def test_head_shard_full_length(gpu_lib, heads):
     """One GPU's share of the 42 heads under head sharding (11/11/10/10) at the 5 s length, through
-    the benchmark's call; at 10 heads the last wave is split, at 11 it is not."""
+    the benchmark's call; the cost model splits the last wave at both (8 and 5 key ranges)."""
     h3 = gpu_lib
     _, segs = W.CONFIGS["5s"]
     n = W.n_tokens(segs)

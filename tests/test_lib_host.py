@@ -158,6 +158,43 @@ def test_abi_rejects_bad_geometry(h3):
     assert fw(P, 1, Q, K, V, O, None, 0, 2, 256, 256, 0.0, None) == 0        # empty: no-op
 
 
+def test_rope_rejects_partial_aliasing(h3):
+    """An output of h3attn_rope_qk may equal its own input (in place) and share no byte with any other
+    tensor.  Every case below fails in the argument checks, before any device call."""
+    lib = h3.load_library()
+    cfg = h3.rope_cfg()
+    P = 1 << 24
+    QI, QO, KI, KO, C = P, 2 * P, 3 * P, 4 * P, 8 * P
+    E = h3.H3ATTN_EINVAL
+    rq = lambda qi, qo, ki, ko, stride=256, c=C: lib.h3attn_rope_qk(ctypes.byref(cfg), c, qi, qo, ki, ko, 64, 2,
+                                                                      stride, None)
+    assert rq(QI, QO, KI, QO) == E                   # both outputs in one place
+    assert rq(QI, QO, KI, QO + 512) == E             # k_out one row behind q_out
+    assert rq(QI, QO, KI, KI + 16) == E              # k_out overlaps its own input without being it
+    assert rq(QI, KI, KI, KO) == E                   # q_out is the other input
+    assert rq(QI, QI + 512, None, None) == E         # q_out shifted by a row from q_in
+    assert rq(QI, QO, KI, QI) == E                   # k_out is q_in
+    assert rq(QI, C, None, None) == E                # an output over the coordinates
+    assert rq(QI, QO, None, None, c=QO + 1024) == E
+    # [N][3][H][128] views (row pitch 1,536 B): Q slot at +0, K slot at +512 B; a K output half a slot
+    # into the Q output's bytes overlaps it
+    assert rq(QI, QO, QI + 512, QO + 256, stride=768) == E
+
+
+def test_rope_accepts_interleaved_views(h3):
+    """In place and interleaved slots of one fused buffer pass the checks; without a GPU the call then
+    stops at the device check (these addresses are never dereferenced on the host)."""
+    if os.path.exists("/dev/kfd"):
+        pytest.skip("a GPU is present: the accepted calls would launch (covered by the GPU tests)")
+    lib = h3.load_library()
+    cfg = h3.rope_cfg()
+    P = 1 << 24
+    rq = lambda qi, qo, ki, ko, stride: lib.h3attn_rope_qk(ctypes.byref(cfg), 8 * P, qi, qo, ki, ko, 64, 2, stride,
+                                                           None)
+    for rc in (rq(P, P, 3 * P, 3 * P, 256), rq(P, 2 * P, P + 512, 2 * P + 512, 768), rq(P, P, P + 512, P + 512, 768)):
+        assert rc in (h3.H3ATTN_EUNSUPPORTED, h3.H3ATTN_EHIP)
+
+
 def test_strerror(h3):
     for code in (0, -1, -2, -3, -4, 99):
         assert isinstance(h3.strerror(code), str) and h3.strerror(code)

@@ -111,10 +111,3 @@ def test_scores_depend_only_on_coordinate_differences():
     c2 = c + np.array([37.0, -5.0, 11.0], np.float32)
     s1 = np.einsum("ihd,jhd->hij", oracle.rope(q, c2, SEC, TH), oracle.rope(k, c2, SEC, TH))
     assert np.max(np.abs(s0 - s1)) < 1e-10
-
-
-def test_inv_freq_table():
-    axes, f = oracle.inv_freq(SEC, TH)
-    assert len(f) == 64 and list(np.bincount(axes)) == [16, 24, 24]
-    assert f[0] == 1.0 and f[16] == 1.0 and f[40] == 1.0
-    assert np.all(np.diff(f[:16]) < 0)
