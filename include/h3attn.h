@@ -13,7 +13,10 @@
  *
  * Conventions for every call:
  *  - All buffers are owned by the caller.  The library allocates no device
- *    memory and keeps no state beyond a per-device cache of device properties.
+ *    memory at run time and keeps no state beyond a per-device cache of device
+ *    properties; the one exception is the static scratch array of
+ *    h3attn_forward_noalloc (H3ATTN_NOALLOC_SCRATCH_BYTES per device, part of
+ *    the loaded code object).
  *  - Device calls are asynchronous on `stream` (a hipStream_t passed as void*;
  *    NULL is the default stream) and never synchronise.
  *  - Arguments are validated before any write or launch: on error nothing has
@@ -38,7 +41,8 @@ enum {
   H3ATTN_EINVAL = -1,       /* null pointer, bad size, bad config, misalignment */
   H3ATTN_ERANGE = -2,       /* capacity too small; coordinate or size out of exact range */
   H3ATTN_EUNSUPPORTED = -3, /* current device is not gfx950 */
-  H3ATTN_EHIP = -4          /* HIP runtime or launch error */
+  H3ATTN_EHIP = -4,         /* HIP runtime or launch error */
+  H3ATTN_ESCRATCH = -5      /* shape needs more than h3attn_forward_noalloc's static scratch */
 };
 
 /* Segment kinds of the packed sequence. */
@@ -305,6 +309,27 @@ int h3attn_forward_ws(const h3attn_rope_cfg* cfg, const float* coords_dev, int32
  * current device (0 when no split pays off, or no gfx950 device is current).
  */
 int64_t h3attn_forward_workspace_bytes(int64_t n_tokens, int32_t n_heads);
+
+/*
+ * Device call for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Arguments, checks and result are those of h3attn_forward_ws given the full
+ * workspace it asks for (the same schedule and kernels, hence the same bits),
+ * but the key-split partials go to a static device array of
+ * H3ATTN_NOALLOC_SCRATCH_BYTES that the library holds on every device it runs
+ * on until the process ends; the call allocates nothing.  A shape whose
+ * partials need more (h3attn_forward_workspace_bytes above the limit; the five
+ * 42-head workloads need at most 64.0 MiB) returns H3ATTN_ESCRATCH before
+ * anything runs.  Every call on one device shares that device's array and
+ * leaves its partials there; nothing in it needs clearing between calls, but
+ * calls in flight at the same time on one device (several streams or host
+ * threads) race on it and must be serialised by the caller.
+ */
+#define H3ATTN_NOALLOC_SCRATCH_BYTES (64LL << 20)
+int h3attn_forward_noalloc(const h3attn_rope_cfg* cfg, const float* coords_dev, int32_t rope_q,
+                           const void* q, const void* k, const void* v, void* o, float* lse,
+                           int64_t n_tokens, int32_t n_heads, int64_t row_stride_qkv,
+                           int64_t row_stride_o, float scale, void* stream);
 
 /* Static description of an error code (never NULL). */
 const char* h3attn_strerror(int code);

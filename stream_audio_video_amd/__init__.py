@@ -20,6 +20,8 @@ device memory and the current stream.  The functions keep the C names:
   forward_ws(cfg, coords_dev, rope_q, q, k, v, o, lse, n_tokens, n_heads, row_stride_qkv, row_stride_o,
              scale, workspace, workspace_bytes, stream=None)
   forward_workspace_bytes(n_tokens, n_heads)
+  forward_noalloc(cfg, coords_dev, rope_q, q, k, v, o, lse, n_tokens, n_heads, row_stride_qkv, row_stride_o,
+                  scale=0.0, stream=None)
   strerror(code), version()
 
 Tensor arguments may be torch tensors (their data_ptr is passed) or raw
@@ -33,14 +35,16 @@ import numpy as np
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libh3attn.so")
 _lib = None
 
-H3ATTN_OK, H3ATTN_EINVAL, H3ATTN_ERANGE, H3ATTN_EUNSUPPORTED, H3ATTN_EHIP = 0, -1, -2, -3, -4
+H3ATTN_OK, H3ATTN_EINVAL, H3ATTN_ERANGE, H3ATTN_EUNSUPPORTED, H3ATTN_EHIP, H3ATTN_ESCRATCH = 0, -1, -2, -3, -4, -5
+NOALLOC_SCRATCH_BYTES = 64 << 20
 SEG_TEXT, SEG_VIDEO, SEG_AUDIO = 0, 1, 2
 LAYER_NORM, RMS_NORM = 0, 1
 ADALN_MAX_HIDDEN = 8192
 
 EXPORTED = ("h3attn_build_coords", "h3attn_rope_qk", "h3attn_forward", "h3attn_adaln_modulate",
             "h3attn_adaln_residual", "h3attn_video_euler_pack", "h3attn_audio_euler_pack", "h3attn_strerror",
-            "h3attn_linear", "h3attn_forward_ws", "h3attn_forward_workspace_bytes", "h3attn_version")
+            "h3attn_linear", "h3attn_forward_ws", "h3attn_forward_workspace_bytes", "h3attn_version",
+            "h3attn_forward_noalloc")
 
 
 class H3AttnError(RuntimeError):
@@ -96,6 +100,9 @@ def load_library(path=None):
     lib.h3attn_forward_ws.argtypes = [ctypes.POINTER(RopeCfg), vp, i32, vp, vp, vp, vp, vp, i64, i32, i64, i64,
                                       ctypes.c_float, vp, i64, vp]
     lib.h3attn_forward_ws.restype = ctypes.c_int
+    lib.h3attn_forward_noalloc.argtypes = [ctypes.POINTER(RopeCfg), vp, i32, vp, vp, vp, vp, vp, i64, i32, i64, i64,
+                                           ctypes.c_float, vp]
+    lib.h3attn_forward_noalloc.restype = ctypes.c_int
     lib.h3attn_forward_workspace_bytes.argtypes = [i64, i32]
     lib.h3attn_forward_workspace_bytes.restype = i64
     lib.h3attn_strerror.argtypes = [ctypes.c_int]
@@ -228,6 +235,15 @@ def forward_ws(cfg, coords_dev, rope_q, q, k, v, o, lse, n_tokens, n_heads, row_
                                 _stream(stream))
     if rc != H3ATTN_OK:
         raise H3AttnError("h3attn_forward_ws", rc)
+
+
+def forward_noalloc(cfg, coords_dev, rope_q, q, k, v, o, lse, n_tokens, n_heads, row_stride_qkv, row_stride_o,
+                    scale=0.0, stream=None):
+    rc = _L().h3attn_forward_noalloc(ctypes.byref(cfg), _ptr(coords_dev), int(rope_q), _ptr(q), _ptr(k), _ptr(v),
+                                     _ptr(o), _ptr(lse), int(n_tokens), int(n_heads), int(row_stride_qkv),
+                                     int(row_stride_o), float(scale), _stream(stream))
+    if rc != H3ATTN_OK:
+        raise H3AttnError("h3attn_forward_noalloc", rc)
 
 
 def forward_workspace_bytes(n_tokens, n_heads):

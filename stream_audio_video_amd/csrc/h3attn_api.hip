@@ -147,7 +147,26 @@ int device_cus() {
 
 int forward_impl(const h3attn_rope_cfg* cfg, const float* coords_dev, int32_t rope_q, const void* q, const void* k,
                  const void* v, void* o, float* lse, int64_t n_tokens, int32_t n_heads, int64_t row_stride_qkv,
-                 int64_t row_stride_o, float scale, void* workspace, int64_t workspace_bytes, void* stream);
+                 int64_t row_stride_o, float scale, void* workspace, int64_t workspace_bytes, bool noalloc, void* stream);
+
+// Scratch of h3attn_forward_noalloc: the key-split partials live in this file-scope device array
+// instead of a caller workspace.  Each device holds its own copy for the life of the process.  In
+// host code the name is only a stand-in for the symbol: kernels receive the device address that
+// hipGetSymbolAddress returns, resolved once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[H3ATTN_NOALLOC_SCRATCH_BYTES];
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// device address of the current device's scratch array, or nullptr when it cannot be resolved
+void* device_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
 
 }  // namespace
 
@@ -165,7 +184,7 @@ extern "C" int h3attn_forward(const h3attn_rope_cfg* cfg, const float* coords_de
                               int64_t n_tokens, int32_t n_heads, int64_t row_stride_qkv,
                               int64_t row_stride_o, float scale, void* stream) {
   return forward_impl(cfg, coords_dev, rope_q, q, k, v, o, lse, n_tokens, n_heads, row_stride_qkv, row_stride_o,
-                      scale, nullptr, 0, stream);
+                      scale, nullptr, 0, false, stream);
 }
 
 extern "C" int h3attn_forward_ws(const h3attn_rope_cfg* cfg, const float* coords_dev, int32_t rope_q,
@@ -176,14 +195,22 @@ extern "C" int h3attn_forward_ws(const h3attn_rope_cfg* cfg, const float* coords
   if (workspace_bytes < 0 || (workspace != nullptr && (reinterpret_cast<uintptr_t>(workspace) & 15u) != 0))
     return H3ATTN_EINVAL;
   return forward_impl(cfg, coords_dev, rope_q, q, k, v, o, lse, n_tokens, n_heads, row_stride_qkv, row_stride_o,
-                      scale, workspace, workspace_bytes, stream);
+                      scale, workspace, workspace_bytes, false, stream);
+}
+
+extern "C" int h3attn_forward_noalloc(const h3attn_rope_cfg* cfg, const float* coords_dev, int32_t rope_q,
+                                      const void* q, const void* k, const void* v, void* o, float* lse,
+                                      int64_t n_tokens, int32_t n_heads, int64_t row_stride_qkv,
+                                      int64_t row_stride_o, float scale, void* stream) {
+  return forward_impl(cfg, coords_dev, rope_q, q, k, v, o, lse, n_tokens, n_heads, row_stride_qkv, row_stride_o,
+                      scale, nullptr, 0, true, stream);
 }
 
 namespace {
 
 int forward_impl(const h3attn_rope_cfg* cfg, const float* coords_dev, int32_t rope_q, const void* q, const void* k,
                  const void* v, void* o, float* lse, int64_t n_tokens, int32_t n_heads, int64_t row_stride_qkv,
-                 int64_t row_stride_o, float scale, void* workspace, int64_t workspace_bytes, void* stream) {
+                 int64_t row_stride_o, float scale, void* workspace, int64_t workspace_bytes, bool noalloc, void* stream) {
   h3::FwdArgs a;
   std::memset(&a, 0, sizeof(a));
   int rc = make_table(cfg, &a.tab);
@@ -220,6 +247,19 @@ int forward_impl(const h3attn_rope_cfg* cfg, const float* coords_dev, int32_t ro
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.rope_q = rope_q ? 1 : 0;
+  if (noalloc) {
+    // the schedule of h3attn_forward_ws with a full workspace; shapes whose partials exceed the
+    // static scratch are refused before anything runs
+    int32_t nf, sp, tps;
+    int64_t need = 0;
+    h3::attn_fwd_schedule(a.n, a.heads, device_cus(), &nf, &sp, &tps, &need);
+    if (need > H3ATTN_NOALLOC_SCRATCH_BYTES) return H3ATTN_ESCRATCH;
+    if (need > 0) {
+      workspace = device_scratch();
+      if (workspace == nullptr) return H3ATTN_EHIP;
+      workspace_bytes = H3ATTN_NOALLOC_SCRATCH_BYTES;
+    }
+  }
   // the key-split tail runs only with a workspace that holds its partials, disjoint from the tensors
   int64_t ws_need = 0;
   h3::attn_fwd_schedule(a.n, a.heads, workspace != nullptr ? device_cus() : 0, &a.n_full, &a.split,
@@ -458,6 +498,7 @@ extern "C" const char* h3attn_strerror(int code) {
     case H3ATTN_ERANGE: return "size or coordinate out of range";
     case H3ATTN_EUNSUPPORTED: return "device is not gfx950";
     case H3ATTN_EHIP: return "HIP runtime error";
+    case H3ATTN_ESCRATCH: return "shape needs more key-split scratch than h3attn_forward_noalloc holds";
     default: return "unknown error";
   }
 }

@@ -195,8 +195,25 @@ def test_rope_accepts_interleaved_views(h3):
         assert rc in (h3.H3ATTN_EUNSUPPORTED, h3.H3ATTN_EHIP)
 
 
+def test_noalloc_rejects_bad_calls(h3):
+    """h3attn_forward_noalloc runs the argument checks of h3attn_forward before anything else."""
+    lib = h3.load_library()
+    cfg = h3.rope_cfg()
+    P = 1 << 20
+    Q, K, V, O = P, 2 * P, 3 * P, 4 * P
+    na = lambda *a: lib.h3attn_forward_noalloc(ctypes.byref(cfg), *a)
+    E = h3.H3ATTN_EINVAL
+    assert na(P, 1, None, K, V, O, None, 64, 2, 256, 256, 0.0, None) == E      # null q
+    assert na(P, 1, Q, K, V, Q, None, 64, 2, 256, 256, 0.0, None) == E         # o aliases q
+    assert na(None, 1, Q, K, V, O, None, 64, 2, 256, 256, 0.0, None) == E      # rope_q without coords
+    assert na(P, 1, Q, K, V, O + 8, None, 64, 2, 256, 256, 0.0, None) == E     # misaligned o
+    assert na(P, 1, Q, K, V, O, None, 2 ** 22, 42, 5376, 5376, 0.0, None) == h3.H3ATTN_ERANGE
+    assert na(P, 1, Q, K, V, O, None, 0, 2, 256, 256, 0.0, None) == 0          # empty: no-op
+    assert "scratch" in h3.strerror(h3.H3ATTN_ESCRATCH)
+
+
 def test_strerror(h3):
-    for code in (0, -1, -2, -3, -4, 99):
+    for code in (0, -1, -2, -3, -4, -5, 99):
         assert isinstance(h3.strerror(code), str) and h3.strerror(code)
 
 
