@@ -112,6 +112,16 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Unit run by full-unit workgroup i of g.  Workgroups are dispatched to the chip's eight
+// XCDs round-robin (workgroup i on XCD i mod 8), and each XCD has its own L2.  XCD x gets the
+// contiguous units [start_x, start_x + cnt_x) in order, so the workgroups resident on one XCD
+// at a time are consecutive query blocks of one head: they read the same K and V tiles, which
+// its L2 then fetches once for all of them.  A bijection on [0, g) for any g.
+__device__ __forceinline__ int xcd_unit(int i, int g) {
+  const int x = i & 7, k = i >> 3;
+  return x * (g >> 3) + min(x, g & 7) + k;
+}
+
 __global__ __launch_bounds__(kThreads, kQB == 1 ? 2 : 1) void attn_fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t ks[kNBuf * kKTile];
   __shared__ __attribute__((aligned(16))) uint16_t vs[kNBuf * kVTile];
@@ -127,7 +137,9 @@ __global__ __launch_bounds__(kThreads, kQB == 1 ? 2 : 1) void attn_fwd_kernel(Fw
   // keys; each later unit is split over `split` workgroups, part p taking key tiles
   // [p * tiles_per_split, ...), and leaves an unnormalised partial result for the merge.
   int unit = blockIdx.x, part = -1, t_begin = 0, t_end = ntiles;
-  if (unit >= a.n_full) {
+  if (unit < a.n_full) {
+    unit = xcd_unit(unit, a.n_full);
+  } else {
     const int r = unit - a.n_full;
     unit = a.n_full + r / a.split;
     part = r - (r / a.split) * a.split;
