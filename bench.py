@@ -96,21 +96,44 @@ WORKLOAD = ("5 s 704x1280 packed sequence: 512 text + 31 latent frames x 22x40 v
             "200 steps x 2 audio = 28,192 tokens; 42 heads x 128; RoPE t/h/w 32/48/48, base 1e4")
 
 
-def cpu_baseline(name, q, k, v, segs, budget_s):
-    """Time the fp64 oracle on a bounded sample: head 0, query rows in blocks of 256, ~budget_s."""
-    import oracle
+def blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:
-        threads = 1
+        return 1
+
+
+def host_record():
+    """The host the oracle ran on: logical CPUs, the ones this process may use, the CPU model and the
+    BLAS thread count (numpy's matrix products use that many threads; its elementwise steps one)."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"cpu_count": os.cpu_count(), "cpus_usable": usable, "cpu_model": model, "blas_threads": blas_threads()}
+
+
+def cpu_baseline(name, q, k, v, segs, budget_s):
+    """Time the fp64 oracle on a bounded sample: head 0, query rows in its default blocks of 1,024
+    rows, for about budget_s seconds (the whole head at 5 s on a 16-CPU host)."""
+    import oracle
+    threads = blas_threads()
     n = q.shape[0]
     c = oracle.build_coords(segs)
     qh = oracle.bf16_bits_to_f64(q[:, :1])
     kh = oracle.bf16_bits_to_f64(k[:, :1])
     vh = oracle.bf16_bits_to_f64(v[:, :1])
     rows_done, t_used = 0, 0.0
-    block = 256
+    block = 1024
     while t_used < budget_s and rows_done < n:
         rows = np.arange(rows_done, min(n, rows_done + block))
         t0 = time.perf_counter()
@@ -118,9 +141,11 @@ def cpu_baseline(name, q, k, v, segs, budget_s):
         t_used += time.perf_counter() - t0
         rows_done += len(rows)
     flops = 4.0 * rows_done * n * W.HEAD_DIM
-    return {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": "%s workload, head 0 of %d, query rows 0..%d against all %d keys (RoPE included), "
-                      "%.1f s of fp64 numpy; FLOP 4*rows*N*D" % (name, q.shape[1], rows_done - 1, n, t_used)}
+    rec = {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+           "sample": "%s workload, head 0 of %d, query rows 0..%d against all %d keys (RoPE included), "
+                     "%.1f s of fp64 numpy; FLOP 4*rows*N*D" % (name, q.shape[1], rows_done - 1, n, t_used)}
+    rec.update(host_record())
+    return rec
 
 
 ADALN_METRIC = "AdaLN gated residual + modulated layer norm GB/s & % HBM peak, 28,192 rows x 5,376"
@@ -145,9 +170,11 @@ def adaln_cpu_baseline(x, y, table, t_idx, tags, budget_s):
         t_used += time.perf_counter() - t0
         rows_done = r.stop
     nbytes = 4 * rows_done * c * 2 + 8 * rows_done
-    return {"value": nbytes / t_used / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "rows 0..%d of %d (blocks of 256), %.1f s of fp64 numpy; bytes 8*rows*C + 8*rows"
-                      % (rows_done - 1, n, t_used)}
+    rec = {"value": nbytes / t_used / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "sample": "rows 0..%d of %d (blocks of 256), %.1f s of fp64 numpy; bytes 8*rows*C + 8*rows"
+                     % (rows_done - 1, n, t_used)}
+    rec.update(host_record())
+    return rec
 
 
 def bench_adaln(args):
@@ -223,8 +250,10 @@ def pack_cpu_baseline(video, v_video, audio, v_audio, dt, budget_s):
         t_used += time.perf_counter() - t0
         reps += 1
     nbytes = 12 * (video.size + audio.size)
-    return {"value": reps * nbytes / t_used / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "%d full steps of the 5 s clip, %.1f s of fp64 numpy" % (reps, t_used)}
+    rec = {"value": reps * nbytes / t_used / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "sample": "%d full steps of the 5 s clip, %.1f s of fp64 numpy" % (reps, t_used)}
+    rec.update(host_record())
+    return rec
 
 
 def bench_pack(args):
@@ -302,14 +331,11 @@ def qkv_cpu_baseline(x, w, b, coords, budget_s):
         t_used += time.perf_counter() - t0
         rows_done = r.stop
     flop = 2.0 * rows_done * w.shape[0] * w.shape[1]
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:
-        threads = 1
-    return {"value": flop / t_used / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": "rows 0..%d of %d (blocks of 64), %.1f s of fp64 numpy; FLOP 2*rows*N*K"
-                      % (rows_done - 1, x.shape[0], t_used)}
+    rec = {"value": flop / t_used / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads()), "kind": "oracle",
+           "sample": "rows 0..%d of %d (blocks of 64), %.1f s of fp64 numpy; FLOP 2*rows*N*K"
+                     % (rows_done - 1, x.shape[0], t_used)}
+    rec.update(host_record())
+    return rec
 
 
 def bench_qkv(args):
@@ -387,11 +413,13 @@ def block_cpu_baseline(config, x, table, t_idx, tags, w_qkv, b_qkv, coords, segs
     ada = adaln_cpu_baseline(x, x, table, t_idx, tags, budget_s / 3)
     secs = (flops["attention"] / (att["value"] * 1e12) + (flops["qkv"] + flops["out_proj"]) / (gem["value"] * 1e12)
             + adaln_b / (ada["value"] * 1e9))
-    return {"value": sum(flops.values()) / secs / 1e12, "unit": "TFLOP/s", "cores": max(att["cores"], gem["cores"]),
-            "kind": "oracle",
-            "sample": "per-stage oracle rates applied to the whole block's FLOP and bytes (AdaLN modulate "
-                      "priced at the residual row's byte rate): attention %s; projections %s; AdaLN %s"
-                      % (att["sample"], gem["sample"], ada["sample"])}
+    rec = {"value": sum(flops.values()) / secs / 1e12, "unit": "TFLOP/s", "cores": max(att["cores"], gem["cores"]),
+           "kind": "oracle",
+           "sample": "per-stage oracle rates applied to the whole block's FLOP and bytes (AdaLN modulate "
+                     "priced at the residual row's byte rate): attention %s; projections %s; AdaLN %s"
+                     % (att["sample"], gem["sample"], ada["sample"])}
+    rec.update(host_record())
+    return rec
 
 
 def bench_block(args):
