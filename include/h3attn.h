@@ -284,6 +284,18 @@ int h3attn_audio_euler_pack(float* latent, int32_t n_ch, int32_t steps, int32_t 
                             const void* v_tokens, int64_t v_stride, float dt, void* tokens,
                             int64_t tokens_stride, void* stream);
 
+/* Both target latents of one sampler step, video and audio, in one launch: the
+ * same result as h3attn_video_euler_pack followed by h3attn_audio_euler_pack
+ * with the same dt, each argument group checked as there.  A part with zero
+ * frames / steps is skipped.  No buffer that one part writes (its latent when
+ * it has velocities, its tokens) may share a byte with a buffer of the other
+ * part (EINVAL). */
+int h3attn_av_euler_pack(float* video_latent, int32_t channels, int32_t frames, int32_t lat_h, int32_t lat_w,
+                         const void* video_v, int64_t video_v_stride, void* video_tokens,
+                         int64_t video_tokens_stride, float* audio_latent, int32_t n_ch, int32_t steps,
+                         int32_t width, const void* audio_v, int64_t audio_v_stride, void* audio_tokens,
+                         int64_t audio_tokens_stride, float dt, void* stream);
+
 /*
  * Device call.  h3attn_forward with a caller-owned scratch workspace (device
  * memory, 16-byte aligned, not overlapping any tensor argument).  The attention

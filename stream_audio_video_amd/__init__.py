@@ -15,6 +15,9 @@ device memory and the current stream.  The functions keep the C names:
   video_euler_pack(latent, channels, frames, lat_h, lat_w, v_tokens, v_stride, dt, tokens, tokens_stride,
                    stream=None)
   audio_euler_pack(latent, n_ch, steps, width, v_tokens, v_stride, dt, tokens, tokens_stride, stream=None)
+  av_euler_pack(video_latent, channels, frames, lat_h, lat_w, video_v, video_v_stride, video_tokens,
+                video_tokens_stride, audio_latent, n_ch, steps, width, audio_v, audio_v_stride, audio_tokens,
+                audio_tokens_stride, dt, stream=None)
   linear(x, x_stride, w, w_stride, bias, y, y_stride, m, n_out, k, rope_cfg=None, coords_dev=None,
          rope_cols=0, stream=None)
   forward_ws(cfg, coords_dev, rope_q, q, k, v, o, lse, n_tokens, n_heads, row_stride_qkv, row_stride_o,
@@ -44,7 +47,7 @@ ADALN_MAX_HIDDEN = 8192
 EXPORTED = ("h3attn_build_coords", "h3attn_rope_qk", "h3attn_forward", "h3attn_adaln_modulate",
             "h3attn_adaln_residual", "h3attn_video_euler_pack", "h3attn_audio_euler_pack", "h3attn_strerror",
             "h3attn_linear", "h3attn_forward_ws", "h3attn_forward_workspace_bytes", "h3attn_version",
-            "h3attn_forward_noalloc")
+            "h3attn_forward_noalloc", "h3attn_av_euler_pack")
 
 
 class H3AttnError(RuntimeError):
@@ -94,6 +97,9 @@ def load_library(path=None):
     lib.h3attn_video_euler_pack.restype = ctypes.c_int
     lib.h3attn_audio_euler_pack.argtypes = [vp, i32, i32, i32, vp, i64, ctypes.c_float, vp, i64, vp]
     lib.h3attn_audio_euler_pack.restype = ctypes.c_int
+    lib.h3attn_av_euler_pack.argtypes = [vp, i32, i32, i32, i32, vp, i64, vp, i64, vp, i32, i32, i32, vp, i64, vp, i64,
+                                         ctypes.c_float, vp]
+    lib.h3attn_av_euler_pack.restype = ctypes.c_int
     lib.h3attn_linear.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, i32, i32, ctypes.POINTER(RopeCfg), vp, i32,
                                   vp]
     lib.h3attn_linear.restype = ctypes.c_int
@@ -216,6 +222,18 @@ def audio_euler_pack(latent, n_ch, steps, width, v_tokens, v_stride, dt, tokens,
                                       int(v_stride), float(dt), _ptr(tokens), int(tokens_stride), _stream(stream))
     if rc != H3ATTN_OK:
         raise H3AttnError("h3attn_audio_euler_pack", rc)
+
+
+def av_euler_pack(video_latent, channels, frames, lat_h, lat_w, video_v, video_v_stride, video_tokens,
+                  video_tokens_stride, audio_latent, n_ch, steps, width, audio_v, audio_v_stride, audio_tokens,
+                  audio_tokens_stride, dt, stream=None):
+    rc = _L().h3attn_av_euler_pack(_ptr(video_latent), int(channels), int(frames), int(lat_h), int(lat_w),
+                                   _ptr(video_v), int(video_v_stride), _ptr(video_tokens), int(video_tokens_stride),
+                                   _ptr(audio_latent), int(n_ch), int(steps), int(width), _ptr(audio_v),
+                                   int(audio_v_stride), _ptr(audio_tokens), int(audio_tokens_stride), float(dt),
+                                   _stream(stream))
+    if rc != H3ATTN_OK:
+        raise H3AttnError("h3attn_av_euler_pack", rc)
 
 
 def linear(x, x_stride, w, w_stride, bias, y, y_stride, m, n_out, k, rope_cfg=None, coords_dev=None, rope_cols=0,

@@ -370,7 +370,8 @@ extern "C" int h3attn_adaln_residual(const void* x, const void* y, int64_t xy_st
 
 namespace {
 
-// Shared checks of the packing calls (sizes already checked by the caller).
+// Shared argument checks of the packing calls (sizes already checked by the caller); the device
+// check comes after every argument check.
 int pack_common(float* latent, int64_t elems, const void* v, int64_t v_stride, void* tokens, int64_t tok_stride,
                 int64_t rows, int64_t width, float dt) {
   if (latent == nullptr || (reinterpret_cast<uintptr_t>(latent) & 7u) != 0) return H3ATTN_EINVAL;
@@ -390,14 +391,23 @@ int pack_common(float* latent, int64_t elems, const void* v, int64_t v_stride, v
     if (overlaps(tokens, tb, latent, lat_bytes)) return H3ATTN_EINVAL;
     if (v != nullptr && overlaps(tokens, tb, v, span_bytes(rows, v_stride, width))) return H3ATTN_EINVAL;
   }
-  return check_device();
+  return H3ATTN_OK;
 }
 
 }  // namespace
 
-extern "C" int h3attn_video_euler_pack(float* latent, int32_t channels, int32_t frames, int32_t lat_h, int32_t lat_w,
-                                       const void* v_tokens, int64_t v_stride, float dt, void* tokens,
-                                       int64_t tokens_stride, void* stream) {
+namespace h3 {
+// one launch for a video and an audio latent (either may be null); pack_kernel.hip
+hipError_t launch_av_pack(const PackArgs* video, const PackArgs* audio, hipStream_t stream);
+}  // namespace h3
+
+namespace {
+
+// Checks of the video packing call; fills a and the byte spans of its buffers.  *rows_out = 0: nothing to do.
+int video_pack_args(float* latent, int32_t channels, int32_t frames, int32_t lat_h, int32_t lat_w,
+                    const void* v_tokens, int64_t v_stride, float dt, void* tokens, int64_t tokens_stride,
+                    h3::PackArgs* a, int64_t* rows_out) {
+  *rows_out = 0;
   if (channels < 1 || frames < 0 || lat_h < 2 || lat_w < 2 || (lat_h & 1) != 0 || (lat_w & 1) != 0)
     return H3ATTN_EINVAL;
   if (int64_t(channels) * 2 * lat_w * 4 > 65536) return H3ATTN_ERANGE;   // two latent rows of every channel in LDS
@@ -405,42 +415,118 @@ extern "C" int h3attn_video_euler_pack(float* latent, int32_t channels, int32_t 
   const int64_t rows = int64_t(frames) * (lat_h / 2) * (lat_w / 2);
   int rc = pack_common(latent, elems, v_tokens, v_stride, tokens, tokens_stride, rows, 4 * int64_t(channels), dt);
   if (rc != H3ATTN_OK || rows == 0) return rc;
+  std::memset(a, 0, sizeof(*a));
+  a->latent = latent;
+  a->v = static_cast<const uint16_t*>(v_tokens);
+  a->tokens = static_cast<uint16_t*>(tokens);
+  a->v_stride = v_stride;
+  a->tok_stride = tokens_stride;
+  a->c = channels;
+  a->t = frames;
+  a->h = lat_h;
+  a->w = lat_w;
+  a->dt = dt;
+  *rows_out = rows;
+  return H3ATTN_OK;
+}
+
+// Checks of the audio packing call; fills a.  *rows_out = 0: nothing to do.
+int audio_pack_args(float* latent, int32_t n_ch, int32_t steps, int32_t width, const void* v_tokens,
+                    int64_t v_stride, float dt, void* tokens, int64_t tokens_stride, h3::PackArgs* a,
+                    int64_t* rows_out) {
+  *rows_out = 0;
+  if (n_ch < 1 || steps < 0 || width < 2 || (width & 1) != 0) return H3ATTN_EINVAL;
+  const int64_t elems = int64_t(n_ch) * steps * width;
+  const int64_t rows = int64_t(n_ch) * steps;
+  int rc = pack_common(latent, elems, v_tokens, v_stride, tokens, tokens_stride, rows, width, dt);
+  if (rc != H3ATTN_OK || rows == 0) return rc;
+  std::memset(a, 0, sizeof(*a));
+  a->latent = latent;
+  a->v = static_cast<const uint16_t*>(v_tokens);
+  a->tokens = static_cast<uint16_t*>(tokens);
+  a->v_stride = v_stride;
+  a->tok_stride = tokens_stride;
+  a->c = n_ch;
+  a->t = steps;
+  a->h = 1;
+  a->w = width;
+  a->dt = dt;
+  *rows_out = rows;
+  return H3ATTN_OK;
+}
+
+// byte spans of a packing call's latent, velocity and token buffers (0 where absent)
+void pack_spans(const h3::PackArgs& a, int64_t rows, int64_t width, int64_t elems, int64_t* lat, int64_t* v,
+                int64_t* tok) {
+  *lat = elems * 4;
+  *v = a.v != nullptr ? span_bytes(rows, a.v_stride, width) : 0;
+  *tok = a.tokens != nullptr ? span_bytes(rows, a.tok_stride, width) : 0;
+}
+
+}  // namespace
+
+extern "C" int h3attn_video_euler_pack(float* latent, int32_t channels, int32_t frames, int32_t lat_h, int32_t lat_w,
+                                       const void* v_tokens, int64_t v_stride, float dt, void* tokens,
+                                       int64_t tokens_stride, void* stream) {
   h3::PackArgs a;
-  std::memset(&a, 0, sizeof(a));
-  a.latent = latent;
-  a.v = static_cast<const uint16_t*>(v_tokens);
-  a.tokens = static_cast<uint16_t*>(tokens);
-  a.v_stride = v_stride;
-  a.tok_stride = tokens_stride;
-  a.c = channels;
-  a.t = frames;
-  a.h = lat_h;
-  a.w = lat_w;
-  a.dt = dt;
+  int64_t rows = 0;
+  int rc = video_pack_args(latent, channels, frames, lat_h, lat_w, v_tokens, v_stride, dt, tokens, tokens_stride, &a,
+                           &rows);
+  if (rc != H3ATTN_OK || rows == 0) return rc;
+  rc = check_device();
+  if (rc != H3ATTN_OK) return rc;
   return h3::launch_video_pack(a, static_cast<hipStream_t>(stream)) == hipSuccess ? H3ATTN_OK : H3ATTN_EHIP;
 }
 
 extern "C" int h3attn_audio_euler_pack(float* latent, int32_t n_ch, int32_t steps, int32_t width,
                                        const void* v_tokens, int64_t v_stride, float dt, void* tokens,
                                        int64_t tokens_stride, void* stream) {
-  if (n_ch < 1 || steps < 0 || width < 2 || (width & 1) != 0) return H3ATTN_EINVAL;
-  const int64_t elems = int64_t(n_ch) * steps * width;
-  const int64_t rows = int64_t(n_ch) * steps;
-  int rc = pack_common(latent, elems, v_tokens, v_stride, tokens, tokens_stride, rows, width, dt);
-  if (rc != H3ATTN_OK || rows == 0) return rc;
   h3::PackArgs a;
-  std::memset(&a, 0, sizeof(a));
-  a.latent = latent;
-  a.v = static_cast<const uint16_t*>(v_tokens);
-  a.tokens = static_cast<uint16_t*>(tokens);
-  a.v_stride = v_stride;
-  a.tok_stride = tokens_stride;
-  a.c = n_ch;
-  a.t = steps;
-  a.h = 1;
-  a.w = width;
-  a.dt = dt;
+  int64_t rows = 0;
+  int rc = audio_pack_args(latent, n_ch, steps, width, v_tokens, v_stride, dt, tokens, tokens_stride, &a, &rows);
+  if (rc != H3ATTN_OK || rows == 0) return rc;
+  rc = check_device();
+  if (rc != H3ATTN_OK) return rc;
   return h3::launch_audio_pack(a, static_cast<hipStream_t>(stream)) == hipSuccess ? H3ATTN_OK : H3ATTN_EHIP;
+}
+
+extern "C" int h3attn_av_euler_pack(float* video_latent, int32_t channels, int32_t frames, int32_t lat_h,
+                                    int32_t lat_w, const void* video_v, int64_t video_v_stride, void* video_tokens,
+                                    int64_t video_tokens_stride, float* audio_latent, int32_t n_ch, int32_t steps,
+                                    int32_t width, const void* audio_v, int64_t audio_v_stride, void* audio_tokens,
+                                    int64_t audio_tokens_stride, float dt, void* stream) {
+  h3::PackArgs va, aa;
+  int64_t vrows = 0, arows = 0;
+  int rc = video_pack_args(video_latent, channels, frames, lat_h, lat_w, video_v, video_v_stride, dt, video_tokens,
+                           video_tokens_stride, &va, &vrows);
+  if (rc != H3ATTN_OK) return rc;
+  rc = audio_pack_args(audio_latent, n_ch, steps, width, audio_v, audio_v_stride, dt, audio_tokens,
+                       audio_tokens_stride, &aa, &arows);
+  if (rc != H3ATTN_OK) return rc;
+  if (vrows == 0 && arows == 0) return H3ATTN_OK;
+  if (vrows > 0 && arows > 0) {
+    // the buffers one part writes (latent, tokens) share no byte with any buffer of the other part
+    int64_t vl, vv, vt, al, av, at;
+    pack_spans(va, vrows, 4 * int64_t(channels), int64_t(channels) * frames * lat_h * lat_w, &vl, &vv, &vt);
+    pack_spans(aa, arows, width, int64_t(n_ch) * steps * width, &al, &av, &at);
+    const void* vb[3] = {va.latent, va.v, va.tokens};
+    const int64_t vn[3] = {vl, vv, vt};
+    const void* ab[3] = {aa.latent, aa.v, aa.tokens};
+    const int64_t an[3] = {al, av, at};
+    const bool v_written[3] = {va.v != nullptr, false, true};   // the latent is written only with velocities
+    const bool a_written[3] = {aa.v != nullptr, false, true};
+    for (int i = 0; i < 3; ++i)
+      for (int j = 0; j < 3; ++j)
+        if (vb[i] != nullptr && ab[j] != nullptr && (v_written[i] || a_written[j]) &&
+            overlaps(vb[i], vn[i], ab[j], an[j]))
+          return H3ATTN_EINVAL;
+  }
+  rc = check_device();
+  if (rc != H3ATTN_OK) return rc;
+  return h3::launch_av_pack(vrows > 0 ? &va : nullptr, arows > 0 ? &aa : nullptr, static_cast<hipStream_t>(stream)) ==
+                 hipSuccess
+             ? H3ATTN_OK
+             : H3ATTN_EHIP;
 }
 
 extern "C" int h3attn_linear(const void* x, int64_t x_stride, const void* w, int64_t w_stride, const void* bias,

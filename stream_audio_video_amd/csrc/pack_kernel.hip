@@ -18,7 +18,11 @@
 // Video: one workgroup per (latent frame, patch row).  The two latent rows of
 // every channel are read coalesced into LDS, updated and emitted in token order
 // (velocity reads and token writes are contiguous rows), then written back
-// coalesced.  HBM-bound: 4 + 4 B of state and 2 + 2 B of tokens per element.
+// coalesced.  HBM-bound: 4 + 4 B of state and 2 + 2 B of tokens per element; at
+// these sizes every workgroup of a launch is resident at once, so the time is the
+// chain of memory round trips of one workgroup.  Audio: one thread per value
+// pair.  One launch can carry both a video and an audio latent (the video
+// workgroups first), which saves the audio launch of a sampler step.
 #include "launch.hpp"
 
 namespace h3 {
@@ -32,10 +36,9 @@ __device__ __forceinline__ f32x2_t bf16x2_to_f32(uint32_t w) {
   return f32x2_t{__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u)};
 }
 
-__global__ __launch_bounds__(kPackThreads) void video_pack_kernel(PackArgs a) {
-  extern __shared__ float tile[];   // [C][2][W]
+__device__ __forceinline__ void video_pack(const PackArgs& a, int blk, float* tile) {
   const int hp = a.h >> 1, wp = a.w >> 1;
-  const int t = blockIdx.x / hp, py = blockIdx.x - t * hp;
+  const int t = blk / hp, py = blk - t * hp;
   const int two_w = 2 * a.w;
   const int n = a.c * two_w;        // elements of the two latent rows, all channels
   const int64_t plane = int64_t(a.t) * a.h * a.w;
@@ -49,7 +52,7 @@ __global__ __launch_bounds__(kPackThreads) void video_pack_kernel(PackArgs a) {
   __syncthreads();
 
   // token order: pair p of token px covers values 2 jp, 2 jp + 1 = (c, iy, ix = 0 / 1)
-  const int64_t row0 = int64_t(blockIdx.x) * wp;
+  const int64_t row0 = int64_t(blk) * wp;
   const int pairs_per_token = 2 * a.c;
   for (int p = threadIdx.x; p < a.c * a.w; p += kPackThreads) {
     const int px = p / pairs_per_token, jp = p - px * pairs_per_token;
@@ -74,10 +77,10 @@ __global__ __launch_bounds__(kPackThreads) void video_pack_kernel(PackArgs a) {
 }
 
 // audio: a = (n_ch, steps, width) in (c, t, w); one thread per value pair
-__global__ __launch_bounds__(kPackThreads) void audio_pack_kernel(PackArgs a) {
+__device__ __forceinline__ void audio_pack(const PackArgs& a, int blk) {
   const int half = a.w >> 1;
   const int64_t total = int64_t(a.t) * a.c * half;
-  const int64_t p = int64_t(blockIdx.x) * kPackThreads + threadIdx.x;
+  const int64_t p = int64_t(blk) * kPackThreads + threadIdx.x;
   if (p >= total) return;
   const int64_t row = p / half;                      // token row s * n_ch + ch
   const int j = 2 * int(p - row * half);
@@ -92,21 +95,41 @@ __global__ __launch_bounds__(kPackThreads) void audio_pack_kernel(PackArgs a) {
   if (a.tokens != nullptr) *reinterpret_cast<uint32_t*>(a.tokens + row * a.tok_stride + j) = pack_bf16x2(v[0], v[1]);
 }
 
+// workgroups [0, video_blocks) pack the video latent, the rest the audio latent
+__global__ __launch_bounds__(kPackThreads) void pack_kernel(PackArgs video, PackArgs audio, int video_blocks) {
+  extern __shared__ float tile[];   // [C][2][W] of the video latent
+  if (static_cast<int>(blockIdx.x) < video_blocks) {
+    video_pack(video, blockIdx.x, tile);
+  } else {
+    audio_pack(audio, blockIdx.x - video_blocks);
+  }
+}
+
 }  // namespace
 
-hipError_t launch_video_pack(const PackArgs& a, hipStream_t stream) {
-  void* args[] = {const_cast<PackArgs*>(&a)};
-  const size_t lds = size_t(a.c) * 2 * a.w * sizeof(float);
-  return hipLaunchKernel(reinterpret_cast<const void*>(&video_pack_kernel), dim3(a.t * (a.h >> 1)),
-                         dim3(kPackThreads), args, lds, stream);
+namespace {
+
+int video_blocks(const PackArgs* v) { return v != nullptr ? v->t * (v->h >> 1) : 0; }
+int audio_blocks(const PackArgs* a) {
+  return a != nullptr ? static_cast<int>((int64_t(a->t) * a->c * (a->w >> 1) + kPackThreads - 1) / kPackThreads) : 0;
 }
 
-hipError_t launch_audio_pack(const PackArgs& a, hipStream_t stream) {
-  void* args[] = {const_cast<PackArgs*>(&a)};
-  const int64_t total = int64_t(a.t) * a.c * (a.w >> 1);
-  return hipLaunchKernel(reinterpret_cast<const void*>(&audio_pack_kernel),
-                         dim3(static_cast<unsigned>((total + kPackThreads - 1) / kPackThreads)), dim3(kPackThreads),
-                         args, 0, stream);
+}  // namespace
+
+hipError_t launch_av_pack(const PackArgs* video, const PackArgs* audio, hipStream_t stream) {
+  PackArgs none;
+  __builtin_memset(&none, 0, sizeof(none));
+  PackArgs v = video != nullptr ? *video : none, au = audio != nullptr ? *audio : none;
+  int vb = video_blocks(video);
+  const int ab = audio_blocks(audio);
+  void* args[] = {&v, &au, &vb};
+  const size_t lds = video != nullptr ? size_t(video->c) * 2 * video->w * sizeof(float) : 0;
+  return hipLaunchKernel(reinterpret_cast<const void*>(&pack_kernel), dim3(vb + ab), dim3(kPackThreads), args, lds,
+                         stream);
 }
+
+hipError_t launch_video_pack(const PackArgs& a, hipStream_t stream) { return launch_av_pack(&a, nullptr, stream); }
+
+hipError_t launch_audio_pack(const PackArgs& a, hipStream_t stream) { return launch_av_pack(nullptr, &a, stream); }
 
 }  // namespace h3

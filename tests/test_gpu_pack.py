@@ -121,3 +121,53 @@ def test_audio_euler_pack(gpu_lib, steps, dt):
     torch.cuda.synchronize()
     assert np.array_equal(host_bits(td), bf16_of_f32(P.pack_audio(lat)))
     assert np.array_equal(ld2.cpu().numpy(), lat)
+
+
+@pytest.mark.parametrize("with_v", [True, False])
+def test_av_pack_equals_separate_calls(gpu_lib, with_v):
+    """Video and audio latents of one sampler step in one launch: bit-equal to the two calls."""
+    h3 = gpu_lib
+    frames, lh, lw, steps = 31, 44, 80, 200
+    c, aw = W.VIDEO_LATENT_CHANNELS, W.AUDIO_LATENT_WIDTH
+    video, v_video, audio, v_audio = W.latent_inputs(frames, lh, lw, steps)
+    dt = 1.0 / 49
+    outs = []
+    for combined in (True, False):
+        vl, al = torch.from_numpy(video.copy()).cuda(), torch.from_numpy(audio.copy()).cuda()
+        vv = dev_bf16(v_video) if with_v else None
+        av = dev_bf16(v_audio) if with_v else None
+        vt = torch.full((v_video.shape[0], 4 * c), 5.0, dtype=torch.bfloat16, device="cuda")
+        at = torch.full((v_audio.shape[0], aw), 5.0, dtype=torch.bfloat16, device="cuda")
+        if combined:
+            h3.av_euler_pack(vl, c, frames, lh, lw, vv, 4 * c, vt, 4 * c, al, 2, steps, aw, av, aw, at, aw, dt)
+        else:
+            h3.video_euler_pack(vl, c, frames, lh, lw, vv, 4 * c, dt, vt, 4 * c)
+            h3.audio_euler_pack(al, 2, steps, aw, av, aw, dt, at, aw)
+        torch.cuda.synchronize()
+        outs.append((vl.cpu().numpy(), al.cpu().numpy(), host_bits(vt), host_bits(at)))
+    for a, b in zip(*outs):
+        assert np.array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
+                              b.view(np.uint32) if b.dtype == np.float32 else b)
+    # and against the oracle: the updated latents and their tokens
+    if with_v:
+        want_v, _ = P.video_euler_pack(video, A.bf16_bits_to_f64(v_video), dt)
+        want_a, _ = P.audio_euler_pack(audio, A.bf16_bits_to_f64(v_audio), dt)
+        check_state(outs[0][0], want_v, "av video")
+        check_state(outs[0][1], want_a, "av audio")
+    else:
+        assert np.array_equal(outs[0][2], bf16_of_f32(P.patchify_video(video)))
+        assert np.array_equal(outs[0][3], bf16_of_f32(P.pack_audio(audio)))
+
+
+def test_av_pack_with_one_part_empty(gpu_lib):
+    """Zero audio steps: the combined call does the video part alone."""
+    h3 = gpu_lib
+    video = np.random.default_rng(3).standard_normal((3, 2, 6, 10)).astype(np.float32)
+    vl = torch.from_numpy(video.copy()).cuda()
+    al = torch.zeros(16, dtype=torch.float32, device="cuda")
+    vt = torch.zeros((2 * 3 * 5, 12), dtype=torch.bfloat16, device="cuda")
+    at = torch.zeros((8, 32), dtype=torch.bfloat16, device="cuda")
+    h3.av_euler_pack(vl, 3, 2, 6, 10, None, 12, vt, 12, al, 2, 0, 32, None, 32, at, 32, 0.1)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(vt), bf16_of_f32(P.patchify_video(video)))
+    assert torch.all(at == 0)

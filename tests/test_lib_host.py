@@ -273,6 +273,26 @@ def test_abi_rejects_bad_pack_calls(h3):
     assert aud(vs=30) == E and aud(ts=33) == E and aud(v=L) == E and aud(t=L) == E
 
 
+def test_abi_rejects_bad_av_pack_calls(h3):
+    """h3attn_av_euler_pack checks each part as the single calls do, and the parts against each other."""
+    lib = h3.load_library()
+    P = 1 << 24
+    VL, VV, VT, AL, AV, AT = P, 4 * P, 8 * P, 12 * P, 13 * P, 14 * P
+    E = h3.H3ATTN_EINVAL
+
+    def av(vl=VL, c=24, f=31, h=44, w=80, vv=VV, vs=96, vt=VT, ts=96, al=AL, ch=2, s=200, aw=32, a_v=AV, avs=32,
+           at=AT, ats=32, dt=0.1):
+        return lib.h3attn_av_euler_pack(vl, c, f, h, w, vv, vs, vt, ts, al, ch, s, aw, a_v, avs, at, ats, dt, None)
+
+    assert av(f=0, s=0) == 0                                 # both parts empty: no-op
+    assert av(h=43) == E and av(aw=31) == E and av(vv=None, vt=None) == E and av(a_v=None, at=None) == E
+    assert av(dt=float("inf")) == E
+    assert av(at=VL + 4096) == E                             # audio tokens inside the video latent
+    assert av(vt=AL) == E                                    # video tokens over the audio latent
+    assert av(al=VV + 64) == E                               # audio latent updated over the video velocities
+    assert av(a_v=VL + 64) == E                              # audio velocities inside the updated video latent
+
+
 def test_abi_rejects_bad_linear_calls(h3):
     lib = h3.load_library()
     cfg = h3.rope_cfg()
