@@ -224,15 +224,17 @@ int h3attn_adaln_residual(const void* x, const void* y, int64_t xy_stride, const
  *
  * Device call.  y = x W^T (+ bias), then, for the leading rope_cols output
  * features (whole 128-wide heads), the rotation of h3attn_rope_qk applied to the
- * float32 results by each row's coordinates, then one rounding to bf16 (nearest
- * even).  For the fused QKV projection of H heads: W is [3 H 128][k] (Q rows,
+ * float32 results with each row's (cos, sin) from a table made by
+ * h3attn_rope_table, then one rounding to bf16 (nearest even).  For the fused QKV projection of H heads: W is [3 H 128][k] (Q rows,
  * then K, then V), rope_cols = 2 H 128, and y = [m][3][H][128] feeds
  * h3attn_forward with rope_q = 0 through strided views (row stride 3 H 128).
  * Readings: no bias unless given; W is stored [n_out][k] (row = output feature).
  *   x          bf16 [m][x_stride], w bf16 [n_out][w_stride], bias bf16 [n_out] or NULL
  *   y          out: bf16 [m][y_stride]; must not overlap x, w or bias
  *   n_out      multiple of H3ATTN_LINEAR_TILE (256);  k multiple of H3ATTN_LINEAR_KSTEP (64)
- *   rope_cfg, coords_dev   as for h3attn_rope_qk; used only when rope_cols > 0
+ *   rope_table_dev  device float32 [m][64][2] from h3attn_rope_table over the
+ *              rows of x, 16-byte aligned; read only when rope_cols > 0 (else may
+ *              be NULL); must not overlap y
  *   rope_cols  0 <= rope_cols <= n_out, multiple of 128
  * Strides are in elements, multiples of 8 (x, w >= k; y >= n_out); pointers
  * 16-byte aligned.  Arithmetic: float32 accumulation of exact bf16 products.
@@ -243,7 +245,23 @@ int h3attn_adaln_residual(const void* x, const void* y, int64_t xy_stride, const
 #define H3ATTN_LINEAR_KSTEP 64
 int h3attn_linear(const void* x, int64_t x_stride, const void* w, int64_t w_stride, const void* bias,
                   void* y, int64_t y_stride, int64_t m, int32_t n_out, int32_t k,
-                  const h3attn_rope_cfg* rope_cfg, const float* coords_dev, int32_t rope_cols, void* stream);
+                  const float* rope_table_dev, int32_t rope_cols, void* stream);
+
+/*
+ * Device call.  The rotation table of a packed sequence: table[i][p] = (cos phi,
+ * sin phi) of pair p of row i, phi = pos_a(i) * theta_a^(-2 p' / d_a) as in
+ * h3attn_rope_qk (same arithmetic, same float32 values), for all 64 pairs of a
+ * 128-wide head.  Every head of Q and K, every block and every sampler step
+ * shares it, so a sequence builds it once (512 B per row, 14.4 MB at 28,192
+ * rows) and h3attn_linear reads it instead of recomputing it per head.
+ *   cfg, coords_dev   as for h3attn_rope_qk
+ *   table_dev         out: device float32 [n_tokens][64][2], 16-byte aligned, not
+ *                     overlapping the coordinates
+ * n_tokens == 0 is a no-op.  Errors: EINVAL, ERANGE (n_tokens * 64 >= 2^31),
+ * EUNSUPPORTED, EHIP.
+ */
+int h3attn_rope_table(const h3attn_rope_cfg* cfg, const float* coords_dev, int64_t n_tokens, float* table_dev,
+                      void* stream);
 
 /*
  * ---- Latent <-> token packing with the sampler's Euler step ----

@@ -18,8 +18,8 @@ device memory and the current stream.  The functions keep the C names:
   av_euler_pack(video_latent, channels, frames, lat_h, lat_w, video_v, video_v_stride, video_tokens,
                 video_tokens_stride, audio_latent, n_ch, steps, width, audio_v, audio_v_stride, audio_tokens,
                 audio_tokens_stride, dt, stream=None)
-  linear(x, x_stride, w, w_stride, bias, y, y_stride, m, n_out, k, rope_cfg=None, coords_dev=None,
-         rope_cols=0, stream=None)
+  linear(x, x_stride, w, w_stride, bias, y, y_stride, m, n_out, k, rope_table=None, rope_cols=0, stream=None)
+  rope_table(cfg, coords_dev, n_tokens, table, stream=None)
   forward_ws(cfg, coords_dev, rope_q, q, k, v, o, lse, n_tokens, n_heads, row_stride_qkv, row_stride_o,
              scale, workspace, workspace_bytes, stream=None)
   forward_workspace_bytes(n_tokens, n_heads)
@@ -47,7 +47,7 @@ ADALN_MAX_HIDDEN = 8192
 EXPORTED = ("h3attn_build_coords", "h3attn_rope_qk", "h3attn_forward", "h3attn_adaln_modulate",
             "h3attn_adaln_residual", "h3attn_video_euler_pack", "h3attn_audio_euler_pack", "h3attn_strerror",
             "h3attn_linear", "h3attn_forward_ws", "h3attn_forward_workspace_bytes", "h3attn_version",
-            "h3attn_forward_noalloc", "h3attn_av_euler_pack")
+            "h3attn_forward_noalloc", "h3attn_av_euler_pack", "h3attn_rope_table")
 
 
 class H3AttnError(RuntimeError):
@@ -100,8 +100,9 @@ def load_library(path=None):
     lib.h3attn_av_euler_pack.argtypes = [vp, i32, i32, i32, i32, vp, i64, vp, i64, vp, i32, i32, i32, vp, i64, vp, i64,
                                          ctypes.c_float, vp]
     lib.h3attn_av_euler_pack.restype = ctypes.c_int
-    lib.h3attn_linear.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, i32, i32, ctypes.POINTER(RopeCfg), vp, i32,
-                                  vp]
+    lib.h3attn_linear.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, i32, i32, vp, i32, vp]
+    lib.h3attn_rope_table.argtypes = [ctypes.POINTER(RopeCfg), vp, i64, vp, vp]
+    lib.h3attn_rope_table.restype = ctypes.c_int
     lib.h3attn_linear.restype = ctypes.c_int
     lib.h3attn_forward_ws.argtypes = [ctypes.POINTER(RopeCfg), vp, i32, vp, vp, vp, vp, vp, i64, i32, i64, i64,
                                       ctypes.c_float, vp, i64, vp]
@@ -236,13 +237,26 @@ def av_euler_pack(video_latent, channels, frames, lat_h, lat_w, video_v, video_v
         raise H3AttnError("h3attn_av_euler_pack", rc)
 
 
-def linear(x, x_stride, w, w_stride, bias, y, y_stride, m, n_out, k, rope_cfg=None, coords_dev=None, rope_cols=0,
-           stream=None):
+def linear(x, x_stride, w, w_stride, bias, y, y_stride, m, n_out, k, rope_table=None, rope_cols=0, stream=None):
     rc = _L().h3attn_linear(_ptr(x), int(x_stride), _ptr(w), int(w_stride), _ptr(bias), _ptr(y), int(y_stride),
-                            int(m), int(n_out), int(k), ctypes.byref(rope_cfg) if rope_cfg is not None else None,
-                            _ptr(coords_dev), int(rope_cols), _stream(stream))
+                            int(m), int(n_out), int(k), _ptr(rope_table), int(rope_cols), _stream(stream))
     if rc != H3ATTN_OK:
         raise H3AttnError("h3attn_linear", rc)
+
+
+def rope_table(cfg, coords_dev, n_tokens, table, stream=None):
+    rc = _L().h3attn_rope_table(ctypes.byref(cfg), _ptr(coords_dev), int(n_tokens), _ptr(table), _stream(stream))
+    if rc != H3ATTN_OK:
+        raise H3AttnError("h3attn_rope_table", rc)
+
+
+def make_rope_table(coords_dev, cfg=None):
+    """Convenience: the rotation table of a sequence, float32 [N, 64, 2], allocated with torch."""
+    import torch
+    n = coords_dev.shape[0]
+    table = torch.empty((n, 64, 2), dtype=torch.float32, device=coords_dev.device)
+    rope_table(cfg or rope_cfg(), coords_dev, n, table)
+    return table
 
 
 def forward_ws(cfg, coords_dev, rope_q, q, k, v, o, lse, n_tokens, n_heads, row_stride_qkv, row_stride_o, scale,

@@ -7,7 +7,10 @@
 // rotating Q and K ("MiniMax H3 - one transformer that denoises video and audio
 // together", position-chain paragraph).  Rotating the projection's float32
 // accumulators before the single rounding to bfloat16 removes the separate
-// RoPE pass over Q and K.
+// RoPE pass over Q and K.  The (cos, sin) of every row's 64 rotation pairs come
+// from a per-sequence table (rope_table_kernel below): the same pairs serve all
+// heads of Q and K, every block and every sampler step, so the epilogue reads
+// them instead of recomputing them per head.
 //
 // Transposed product, C^T[feature][token] = W . x^T on v_mfma_f32_32x32x16_bf16
 // (A = W rows, B = x rows, both k-contiguous).  Each lane then holds one token
@@ -48,8 +51,11 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8;
+typedef __attribute__((address_space(3))) u32x2_t lds_u32x2;
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
@@ -206,11 +212,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs a) {
   if (s + 1 < nst) stage(s++, True{}, False{});
   stage(s, False{}, False{});
 
-  // epilogue: bias, rotation of whole-head slabs, one rounding to bf16.  Everything it reads from
-  // memory is requested up front so that the latencies overlap: the lane's 64 bias values (the same
-  // for every token block), its 4 tokens' coordinates, and the rotation table through wave-uniform
-  // indices (scalar loads; the lane's half hf then selects between two candidate pairs).  Nothing
-  // is hoisted across token blocks: more live state here makes the allocator spill accumulators.
+  // epilogue: bias, rotation of whole-head slabs by the rows' (cos, sin) from the table, one rounding
+  // to bf16.  The lane's 64 bias values are the same for every token block and are requested first.
   const int fw0 = f0 + wf * 128;                       // first feature of this wave: a head boundary
   const bool rotate = fw0 < a.rope_cols;
   uint2 bw[4][4];
@@ -220,37 +223,30 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs a) {
     for (int g = 0; g < 4; ++g)
       bw[fb][g] = a.bias != nullptr ? *reinterpret_cast<const uint2*>(a.bias + fw0 + fb * 32 + 8 * g + 4 * hf)
                                     : make_uint2(0, 0);
-  // the lane's 4 tokens' coordinates through a descriptor over this wave's token rows (rows past
-  // m read as zero), and the output through one over the same rows (their stores are dropped)
+  // the output through a descriptor over this wave's token rows (rows past m: stores dropped), and
+  // the rotation table through one over the same rows (rows past m read as zero)
   const int tw0 = t0 + wt * 128;
   const int rows = min(a.m - tw0, 128);                // may be <= 0 on the last token tile
   const int yrow_bytes = static_cast<int>(a.y_stride * 2);
-  float pos[4][3];
-  if (rotate) {
-    const __amdgpu_buffer_rsrc_t cd = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(a.coords) + 3 * int64_t(tw0), 0, rows > 0 ? rows * 12 : 0, kRsrcFlags);
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-      for (int ax = 0; ax < 3; ++ax)
-        pos[tb][ax] =
-            __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(cd, (tb * 32 + col) * 12 + 4 * ax, 0, 0));
-  }
   const __amdgpu_buffer_rsrc_t yd = __builtin_amdgcn_make_buffer_rsrc(
       a.y + int64_t(tw0) * a.y_stride + fw0, 0, rows > 0 ? (rows - 1) * yrow_bytes + 256 : 0, kRsrcFlags);
-  // cos / sin of the lane's rotation pair at register slot (fb, g, h) for token block tb
-  auto angle = [&](int tb, int fb, int g, int h, float& cs, float& sn) {
-    const int u = fb * 16 + 4 * g + h;                 // pair of this register pair at hf = 0; + 2 at hf = 1
-    const double f_lo = a.tab.freq[u], f_hi = a.tab.freq[u + 2];
-    const int ax_lo = rope_axis(u, a.tab), ax_hi = rope_axis(u + 2, a.tab);
-    const int ax = hf ? ax_hi : ax_lo;
-    float p = ax == 1 ? pos[tb][1] : pos[tb][2];       // two selects, not a branch
-    p = ax == 0 ? pos[tb][0] : p;
-    rope_cos_sin(p, hf ? f_hi : f_lo, cs, sn);
+  const __amdgpu_buffer_rsrc_t td = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(a.rope_tab) + int64_t(tw0) * (2 * kPairs), 0, rotate && rows > 0 ? rows * kPairs * 8 : 0,
+      kRsrcFlags);
+  // (cos, sin) of the lane's pairs fb 16 + 4 g + 2 hf and the next one, token block tb: 16 bytes
+  auto rot4 = [&](int tb, int fb, int g) {
+    return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                          td, ((tb * 32 + col) * kPairs + fb * 16 + 4 * g + 2 * hf) * 8, 0, 0));
   };
+  // The bf16 results go through this wave's 32 KB of LDS (free once every wave is past the last
+  // barrier: the final k-step reads only registers), token-major with 256 B per token, so that
+  // each store instruction then writes four whole output rows instead of 16 B of 32 rows.  The
+  // 16-byte chunk c of token row r sits at slot c ^ (r & 15), which keeps the row-segment reads
+  // on disjoint banks.
+  lds_u16* eb = (wave < 2 ? (lds_u16*)as : (lds_u16*)bs) + (wave & 1) * (128 * 128);
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb) {
-    const int yrow = (tb * 32 + col) * yrow_bytes;
+    const int erow = tb * 32 + col;
 #pragma unroll
     for (int fb = 0; fb < 4; ++fb) {
       f32x16_t v = acc[fb][tb];
@@ -262,23 +258,51 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs a) {
         v[4 * g + 2] += __uint_as_float(bw[fb][g].y << 16);
         v[4 * g + 3] += __uint_as_float(bw[fb][g].y & 0xffff0000u);
         if (rotate) {
+          const float4 r = rot4(tb, fb, g);
+          const float cs[2] = {r.x, r.z}, sn[2] = {r.y, r.w};
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
-            float cs, sn;
-            angle(tb, fb, g, h, cs, sn);
             const float x = v[4 * g + 2 * h], y = v[4 * g + 2 * h + 1];
-            v[4 * g + 2 * h] = __builtin_fmaf(x, cs, -(y * sn));
-            v[4 * g + 2 * h + 1] = __builtin_fmaf(x, sn, y * cs);
+            v[4 * g + 2 * h] = __builtin_fmaf(x, cs[h], -(y * sn[h]));
+            v[4 * g + 2 * h + 1] = __builtin_fmaf(x, sn[h], y * cs[h]);
           }
         }
         const uint2 w = make_uint2(pack_bf16x2(v[4 * g + 0], v[4 * g + 1]), pack_bf16x2(v[4 * g + 2], v[4 * g + 3]));
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, w), yd, yrow + d0 * 2, 0, 0);
+        const int slot = (d0 >> 3) ^ (erow & 15);
+        *reinterpret_cast<lds_u32x2*>(eb + erow * 128 + slot * 8 + 4 * hf) = u32x2_t{w.x, w.y};
       }
     }
   }
+  // row segments out: instruction j covers token rows 4 j .. 4 j + 3, lane l the 16-byte chunk l & 15
+  // of row 4 j + (l >> 4); a wave's LDS writes complete in order before its reads
+  const int sc = lane & 15;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const int r = 4 * j + (lane >> 4);
+    const u32x4_t w = *reinterpret_cast<const lds_u32x4*>(eb + r * 128 + (sc ^ (r & 15)) * 8);
+    __builtin_amdgcn_raw_buffer_store_b128(w, yd, r * yrow_bytes + sc * 16, 0, 0);
+  }
+}
+
+// (cos, sin) of pair p of row i, one thread per (row, pair), with the rotation arithmetic every RoPE
+// route shares (rope_math.hpp): the values the streaming pass and the attention's Q load use.
+__global__ __launch_bounds__(256) void rope_table_kernel(RopeTabArgs a) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= int64_t(a.n) * kPairs) return;
+  const int row = static_cast<int>(i / kPairs), pair = static_cast<int>(i - int64_t(row) * kPairs);
+  float c, s;
+  rope_cos_sin(a.coords[3 * int64_t(row) + rope_axis(pair, a.tab)], a.tab.freq[pair], c, s);
+  reinterpret_cast<float2*>(a.out)[i] = make_float2(c, s);
 }
 
 }  // namespace
+
+hipError_t launch_rope_table(const RopeTabArgs& a, hipStream_t stream) {
+  const int64_t total = int64_t(a.n) * kPairs;
+  void* args[] = {const_cast<RopeTabArgs*>(&a)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&rope_table_kernel),
+                         dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), args, 0, stream);
+}
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
   void* args[] = {const_cast<GemmArgs*>(&a)};

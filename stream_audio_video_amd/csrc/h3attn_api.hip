@@ -529,10 +529,30 @@ extern "C" int h3attn_av_euler_pack(float* video_latent, int32_t channels, int32
              : H3ATTN_EHIP;
 }
 
+extern "C" int h3attn_rope_table(const h3attn_rope_cfg* cfg, const float* coords_dev, int64_t n_tokens,
+                                 float* table_dev, void* stream) {
+  h3::RopeTabArgs a;
+  std::memset(&a, 0, sizeof(a));
+  int rc = make_table(cfg, &a.tab);
+  if (rc != H3ATTN_OK) return rc;
+  if (n_tokens < 0) return H3ATTN_EINVAL;
+  if (n_tokens >= (int64_t(1) << 31) / h3::kPairs) return H3ATTN_ERANGE;
+  if (n_tokens == 0) return H3ATTN_OK;
+  if (coords_dev == nullptr || table_dev == nullptr || !aligned16(table_dev) ||
+      (reinterpret_cast<uintptr_t>(coords_dev) & 3u) != 0)
+    return H3ATTN_EINVAL;
+  if (overlaps(table_dev, n_tokens * h3::kPairs * 8, coords_dev, n_tokens * 12)) return H3ATTN_EINVAL;
+  rc = check_device();
+  if (rc != H3ATTN_OK) return rc;
+  a.coords = coords_dev;
+  a.out = table_dev;
+  a.n = static_cast<int32_t>(n_tokens);
+  return h3::launch_rope_table(a, static_cast<hipStream_t>(stream)) == hipSuccess ? H3ATTN_OK : H3ATTN_EHIP;
+}
+
 extern "C" int h3attn_linear(const void* x, int64_t x_stride, const void* w, int64_t w_stride, const void* bias,
                              void* y, int64_t y_stride, int64_t m, int32_t n_out, int32_t k,
-                             const h3attn_rope_cfg* rope_cfg, const float* coords_dev, int32_t rope_cols,
-                             void* stream) {
+                             const float* rope_table_dev, int32_t rope_cols, void* stream) {
   h3::GemmArgs a;
   std::memset(&a, 0, sizeof(a));
   if (x == nullptr || w == nullptr || y == nullptr) return H3ATTN_EINVAL;
@@ -543,11 +563,7 @@ extern "C" int h3attn_linear(const void* x, int64_t x_stride, const void* w, int
       (y_stride & 7) != 0)
     return H3ATTN_EINVAL;
   if (rope_cols < 0 || rope_cols > n_out || (rope_cols % h3::kHeadDim) != 0) return H3ATTN_EINVAL;
-  if (rope_cols > 0) {
-    int rc = make_table(rope_cfg, &a.tab);
-    if (rc != H3ATTN_OK) return rc;
-    if (coords_dev == nullptr) return H3ATTN_EINVAL;
-  }
+  if (rope_cols > 0 && (rope_table_dev == nullptr || !aligned16(rope_table_dev))) return H3ATTN_EINVAL;
   // byte offsets inside a 256-row tile and over x are 32-bit
   if (m >= (int64_t(1) << 31) || int64_t(H3ATTN_LINEAR_TILE) * x_stride * 2 >= (int64_t(1) << 31) ||
       int64_t(H3ATTN_LINEAR_TILE) * w_stride * 2 >= (int64_t(1) << 31) ||
@@ -556,7 +572,8 @@ extern "C" int h3attn_linear(const void* x, int64_t x_stride, const void* w, int
   if (m == 0) return H3ATTN_OK;
   const int64_t yb = span_bytes(m, y_stride, n_out);
   if (overlaps(y, yb, x, span_bytes(m, x_stride, k)) || overlaps(y, yb, w, span_bytes(n_out, w_stride, k)) ||
-      (bias != nullptr && overlaps(y, yb, bias, int64_t(n_out) * 2)))
+      (bias != nullptr && overlaps(y, yb, bias, int64_t(n_out) * 2)) ||
+      (rope_cols > 0 && overlaps(y, yb, rope_table_dev, m * h3::kPairs * 8)))
     return H3ATTN_EINVAL;
   int rc = check_device();
   if (rc != H3ATTN_OK) return rc;
@@ -564,7 +581,7 @@ extern "C" int h3attn_linear(const void* x, int64_t x_stride, const void* w, int
   a.w = static_cast<const uint16_t*>(w);
   a.bias = static_cast<const uint16_t*>(bias);
   a.y = static_cast<uint16_t*>(y);
-  a.coords = coords_dev;
+  a.rope_tab = rope_table_dev;
   a.x_stride = x_stride;
   a.w_stride = w_stride;
   a.y_stride = y_stride;

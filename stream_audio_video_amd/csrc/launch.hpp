@@ -83,7 +83,7 @@ struct GemmArgs {
   const uint16_t* w;       // bf16 [n_out][w_stride]
   const uint16_t* bias;    // bf16 [n_out] or null
   uint16_t* y;             // bf16 [m][y_stride]
-  const float* coords;     // [m][3] when rope_cols > 0
+  const float* rope_tab;   // [m][64][2] (cos, sin) of every row's rotation pairs when rope_cols > 0
   int64_t x_stride;
   int64_t w_stride;
   int64_t y_stride;
@@ -93,11 +93,18 @@ struct GemmArgs {
   int32_t rope_cols;       // leading output features rotated, in whole 128-wide heads
   int32_t tiles_f;
   int32_t tiles_t;
+};
+
+struct RopeTabArgs {
+  const float* coords;     // [n][3]
+  float* out;              // [n][64][2]: (cos, sin) of pair p of row i
+  int32_t n;
   RopeTable tab;
 };
 
 hipError_t launch_rope_qk(const RopeArgs& a, hipStream_t stream);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_rope_table(const RopeTabArgs& a, hipStream_t stream);
 hipError_t launch_video_pack(const PackArgs& a, hipStream_t stream);
 hipError_t launch_audio_pack(const PackArgs& a, hipStream_t stream);
 hipError_t launch_adaln(const AdalnArgs& a, hipStream_t stream);

@@ -76,7 +76,7 @@ def test_attention_half_block(gpu_lib, kind):
     h1 = torch.empty_like(xd)
     h3.adaln_modulate(xd, c, ti, tg, base, base + 2 * c, 6 * c, table.shape[0], h1, c, n, c, kind, EPS)
     qkv = torch.empty((n, 3, heads, 128), dtype=torch.bfloat16, device="cuda")
-    h3.linear(h1, c, dev_bf16(w_qkv), c, dev_bf16(b_qkv), qkv, 3 * c, n, 3 * c, c, h3.rope_cfg(), coords, 2 * c)
+    h3.linear(h1, c, dev_bf16(w_qkv), c, dev_bf16(b_qkv), qkv, 3 * c, n, 3 * c, c, h3.make_rope_table(coords), 2 * c)
     o = torch.empty((n, heads, 128), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((heads, n), dtype=torch.float32, device="cuda")
     need = h3.forward_workspace_bytes(n, heads)

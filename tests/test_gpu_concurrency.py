@@ -31,6 +31,7 @@ def make_problem(h3, seed, n_text, frames, heads):
          "q": dev_bf16(q), "k": dev_bf16(k), "v": dev_bf16(v), "x": dev_bf16(x), "w": dev_bf16(w),
          "b": dev_bf16(b)}
     p["kr"] = torch.empty_like(p["k"])
+    p["table"] = h3.make_rope_table(p["coords"])
     p["o"] = torch.empty_like(p["q"])
     p["lse"] = torch.empty((heads, n), dtype=torch.float32, device="cuda")
     p["y"] = torch.empty((n, 512), dtype=torch.bfloat16, device="cuda")
@@ -46,7 +47,7 @@ def run_problem(h3, p, stream):
     h3.rope_qk(cfg, p["coords"], None, None, p["k"], p["kr"], n, heads, stride, stream=stream)
     h3.forward_ws(cfg, p["coords"], 1, p["q"], p["kr"], p["v"], p["o"], p["lse"], n, heads, stride, stride, 0.0,
                   p["ws"], p["ws_bytes"], stream=stream)
-    h3.linear(p["x"], 256, p["w"], 256, p["b"], p["y"], 512, n, 512, 256, cfg, p["coords"], 256, stream=stream)
+    h3.linear(p["x"], 256, p["w"], 256, p["b"], p["y"], 512, n, 512, 256, p["table"], 256, stream=stream)
 
 
 def snapshot(p):

@@ -74,7 +74,8 @@ def run(h3, x, w, b, m, n, k, rope_cols=0, coords=None, x_stride=None, y_stride=
     wd = dev_bf16(w)
     bd = dev_bf16(b) if b is not None else None
     yd = torch.full((m, ys), 3.0, dtype=torch.bfloat16, device="cuda")
-    h3.linear(xd, xs, wd, k, bd, yd, ys, m, n, k, h3.rope_cfg() if rope_cols else None, coords, rope_cols)
+    table = h3.make_rope_table(coords) if rope_cols else None
+    h3.linear(xd, xs, wd, k, bd, yd, ys, m, n, k, table, rope_cols)
     torch.cuda.synchronize()
     return host_bits(yd)
 
@@ -122,8 +123,8 @@ def test_rows_past_m_untouched(gpu_lib, rope):
     x, w, b = W.projection_inputs(m, k, n, seed=41)
     coords_h = gpu_lib.build_coords(segs_of(m))
     yd = torch.full((m + 300, n), 3.0, dtype=torch.bfloat16, device="cuda")
-    gpu_lib.linear(dev_bf16(x), k, dev_bf16(w), k, dev_bf16(b), yd, n, m, n, k,
-                   gpu_lib.rope_cfg() if rope else None, torch.from_numpy(coords_h).cuda() if rope else None,
+    table = gpu_lib.make_rope_table(torch.from_numpy(coords_h).cuda()) if rope else None
+    gpu_lib.linear(dev_bf16(x), k, dev_bf16(w), k, dev_bf16(b), yd, n, m, n, k, table,
                    2 * heads * 128 if rope else 0)
     torch.cuda.synchronize()
     y = host_bits(yd)
@@ -158,7 +159,8 @@ def test_projection_feeds_attention(gpu_lib):
     coords_h = h3.build_coords(segs)
     coords = torch.from_numpy(coords_h).cuda()
     yd = torch.empty((m, 3, heads, 128), dtype=torch.bfloat16, device="cuda")
-    h3.linear(dev_bf16(x), k, dev_bf16(w), k, dev_bf16(b), yd, n, m, n, k, h3.rope_cfg(), coords, 2 * heads * 128)
+    h3.linear(dev_bf16(x), k, dev_bf16(w), k, dev_bf16(b), yd, n, m, n, k, h3.make_rope_table(coords),
+              2 * heads * 128)
     o = torch.empty((m, heads, 128), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((heads, m), dtype=torch.float32, device="cuda")
     h3.forward(h3.rope_cfg(), coords, 0, yd[:, 0], yd[:, 1], yd[:, 2], o, lse, m, heads, n, heads * 128)
@@ -171,3 +173,25 @@ def test_projection_feeds_attention(gpu_lib):
     print("chain max|err| %.3e rms %.3e" % (np.abs(err).max(), np.sqrt((err ** 2).mean())), flush=True)
     assert np.abs(err).max() <= 2e-2 and np.sqrt((err ** 2).mean()) <= 2e-3
     assert np.abs(lse.cpu().numpy() - lse_ref).max() <= 1e-2
+
+
+@pytest.mark.parametrize("cfg_name", ["5s", "tiny"])
+def test_rope_table_matches_oracle(gpu_lib, cfg_name):
+    """h3attn_rope_table: (cos, sin) of every row and pair.  The oracle rotates the unit vector (1, 0) of
+    each pair, which gives (cos phi, sin phi) in float64; the kernel's float32 values are within
+    6e-8 (angle reduced in float64, then a float32 polynomial) -- test 2.5e-7 absolute."""
+    h3 = gpu_lib
+    _, segs = W.CONFIGS[cfg_name]
+    coords_h = h3.build_coords(segs)
+    n = coords_h.shape[0]
+    table = torch.full((n + 8, 64, 2), 7.0, dtype=torch.float32, device="cuda")
+    h3.rope_table(h3.rope_cfg(), torch.from_numpy(coords_h).cuda(), n, table)
+    torch.cuda.synchronize()
+    got = table.cpu().numpy().astype(np.float64)
+    assert np.all(got[n:] == 7.0)                                         # rows past n untouched
+    unit = np.zeros((n, 1, 128))
+    unit[:, :, 0::2] = 1.0
+    ref = oracle.rope(unit, coords_h, SEC, TH)[:, 0].reshape(n, 64, 2)   # (cos, sin) per pair
+    err = np.abs(got[:n] - ref)
+    print("%s table max|err| %.3e" % (cfg_name, float(err.max())), flush=True)
+    assert err.max() <= 2.5e-7

@@ -293,16 +293,32 @@ def test_abi_rejects_bad_av_pack_calls(h3):
     assert av(a_v=VL + 64) == E                              # audio velocities inside the updated video latent
 
 
-def test_abi_rejects_bad_linear_calls(h3):
+def test_abi_rejects_bad_rope_table_calls(h3):
     lib = h3.load_library()
     cfg = h3.rope_cfg()
     P = 1 << 26
-    X, Wt, B, Y, C = P, 4 * P, 8 * P, 12 * P, 16 * P
+    C, T = P, 4 * P
     E, R = h3.H3ATTN_EINVAL, h3.H3ATTN_ERANGE
 
-    def lin(x=X, xs=5376, w=Wt, ws=5376, b=B, y=Y, ys=16128, m=28192, n=16128, k=5376, cf=cfg, c=C, rc=10752):
-        return lib.h3attn_linear(x, xs, w, ws, b, y, ys, m, n, k, ctypes.byref(cf) if cf is not None else None, c, rc,
-                                 None)
+    def tab(cf=cfg, c=C, n=28192, t=T):
+        return lib.h3attn_rope_table(ctypes.byref(cf) if cf is not None else None, c, n, t, None)
+
+    assert tab(n=0) == 0                                     # empty: no-op
+    assert tab(cf=None) == E and tab(cf=_cfg(h3, head_dim=64)) == E
+    assert tab(c=None) == E and tab(t=None) == E and tab(t=T + 8) == E and tab(c=C + 2) == E and tab(n=-1) == E
+    assert tab(t=C + 4096) == E                              # table over the coordinates
+    assert tab(n=2 ** 25) == R                               # n * 64 pairs reach 2^31
+    assert tab() not in (E, R)                               # valid: fails only for want of a GPU
+
+
+def test_abi_rejects_bad_linear_calls(h3):
+    lib = h3.load_library()
+    P = 1 << 26
+    X, Wt, B, Y, T = P, 4 * P, 8 * P, 12 * P, 16 * P
+    E, R = h3.H3ATTN_EINVAL, h3.H3ATTN_ERANGE
+
+    def lin(x=X, xs=5376, w=Wt, ws=5376, b=B, y=Y, ys=16128, m=28192, n=16128, k=5376, t=T, rc=10752):
+        return lib.h3attn_linear(x, xs, w, ws, b, y, ys, m, n, k, t, rc, None)
 
     assert lin(m=0) == 0                                     # empty: no-op
     assert lin(x=None) == E and lin(w=None) == E and lin(y=None) == E
@@ -310,8 +326,9 @@ def test_abi_rejects_bad_linear_calls(h3):
     assert lin(n=16000) == E and lin(k=5370) == E and lin(k=0) == E and lin(n=0) == E and lin(m=-1) == E
     assert lin(xs=5368) == E and lin(ws=5380) == E and lin(ys=16120) == E
     assert lin(rc=100) == E and lin(rc=16384) == E and lin(rc=-128) == E
-    assert lin(cf=None) == E and lin(c=None) == E            # rotation without its configuration
-    assert lin(cf=_cfg(h3, head_dim=64)) == E
+    assert lin(t=None) == E and lin(t=T + 8) == E           # rotation without its table, misaligned table
+    assert lin(t=None, rc=0) not in (E, R)                   # no rotation: no table needed (fails later: no GPU)
+    assert lin(t=Y + 16128 * 2 * 100) == E                   # y overlaps the table
     assert lin(y=X + 4096) == E and lin(y=Wt) == E and lin(b=Y + 64) == E   # y overlaps an input
     assert lin(xs=2 ** 22 + 8) == R                          # a 256-row tile of x spans 2^31 bytes
     assert lin(ys=2 ** 22) == R and lin(ws=2 ** 22) == R      # ... of y, of w
