@@ -65,6 +65,7 @@ constexpr int kBuf = kTile * kBK;             // elements per operand stage
 constexpr int kRowsPerWave = kTile / kWaves;  // rows of each operand a wave loads per stage (64)
 constexpr int kEarly = 8;                     // loads of a stage issued as soon as its buffer is free
 constexpr int kGroup = 4;                     // token tiles per ordering group
+constexpr int kAhead = 4;                     // epilogue table loads in flight, in (token, feature) block steps
 constexpr int kRsrcFlags = 0x00020000;        // raw buffer, 32-bit data format
 static_assert(kEarly >= 0 && kEarly <= 8, "at most one load per MFMA");
 
@@ -216,13 +217,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs a) {
   // to bf16.  The lane's 64 bias values are the same for every token block and are requested first.
   const int fw0 = f0 + wf * 128;                       // first feature of this wave: a head boundary
   const bool rotate = fw0 < a.rope_cols;
+  // Every epilogue load is unconditional (a missing bias, or a slab without rotation, reads zeros
+  // through an empty descriptor), so the waits before their uses are counted, never a vmcnt(0) at a
+  // branch merge.
+  const __amdgpu_buffer_rsrc_t bd = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.bias != nullptr ? a.bias + fw0 : a.y), 0, a.bias != nullptr ? 256 : 0, kRsrcFlags);
   uint2 bw[4][4];
 #pragma unroll
   for (int fb = 0; fb < 4; ++fb)
 #pragma unroll
     for (int g = 0; g < 4; ++g)
-      bw[fb][g] = a.bias != nullptr ? *reinterpret_cast<const uint2*>(a.bias + fw0 + fb * 32 + 8 * g + 4 * hf)
-                                    : make_uint2(0, 0);
+      bw[fb][g] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(bd, (fb * 32 + 8 * g + 4 * hf) * 2, 0, 0));
   // the output through a descriptor over this wave's token rows (rows past m: stores dropped), and
   // the rotation table through one over the same rows (rows past m read as zero)
   const int tw0 = t0 + wt * 128;
@@ -244,33 +249,40 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs a) {
   // 16-byte chunk c of token row r sits at slot c ^ (r & 15), which keeps the row-segment reads
   // on disjoint banks.
   lds_u16* eb = (wave < 2 ? (lds_u16*)as : (lds_u16*)bs) + (wave & 1) * (128 * 128);
+  // The table loads run kAhead (token block, feature block) steps ahead of their use.
+  float4 rt[kAhead + 1][4];
+  auto fetch = [&](int i) {                            // step i = 4 tb + fb
 #pragma unroll
-  for (int tb = 0; tb < 4; ++tb) {
+    for (int g = 0; g < 4; ++g) rt[i % (kAhead + 1)][g] = rot4(i >> 2, i & 3, g);
+  };
+#pragma unroll
+  for (int i = 0; i < kAhead; ++i) fetch(i);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int tb = i >> 2, fb = i & 3;
+    if (i + kAhead < 16) fetch(i + kAhead);
     const int erow = tb * 32 + col;
+    f32x16_t v = acc[fb][tb];
 #pragma unroll
-    for (int fb = 0; fb < 4; ++fb) {
-      f32x16_t v = acc[fb][tb];
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = fb * 32 + 8 * g + 4 * hf;         // head-dim index of register 4 g
+      v[4 * g + 0] += __uint_as_float(bw[fb][g].x << 16);
+      v[4 * g + 1] += __uint_as_float(bw[fb][g].x & 0xffff0000u);
+      v[4 * g + 2] += __uint_as_float(bw[fb][g].y << 16);
+      v[4 * g + 3] += __uint_as_float(bw[fb][g].y & 0xffff0000u);
+      if (rotate) {
+        const float4 r = rt[i % (kAhead + 1)][g];
+        const float cs[2] = {r.x, r.z}, sn[2] = {r.y, r.w};
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = fb * 32 + 8 * g + 4 * hf;       // head-dim index of register 4 g
-        v[4 * g + 0] += __uint_as_float(bw[fb][g].x << 16);
-        v[4 * g + 1] += __uint_as_float(bw[fb][g].x & 0xffff0000u);
-        v[4 * g + 2] += __uint_as_float(bw[fb][g].y << 16);
-        v[4 * g + 3] += __uint_as_float(bw[fb][g].y & 0xffff0000u);
-        if (rotate) {
-          const float4 r = rot4(tb, fb, g);
-          const float cs[2] = {r.x, r.z}, sn[2] = {r.y, r.w};
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const float x = v[4 * g + 2 * h], y = v[4 * g + 2 * h + 1];
-            v[4 * g + 2 * h] = __builtin_fmaf(x, cs[h], -(y * sn[h]));
-            v[4 * g + 2 * h + 1] = __builtin_fmaf(x, sn[h], y * cs[h]);
-          }
+        for (int h = 0; h < 2; ++h) {
+          const float x = v[4 * g + 2 * h], y = v[4 * g + 2 * h + 1];
+          v[4 * g + 2 * h] = __builtin_fmaf(x, cs[h], -(y * sn[h]));
+          v[4 * g + 2 * h + 1] = __builtin_fmaf(x, sn[h], y * cs[h]);
         }
-        const uint2 w = make_uint2(pack_bf16x2(v[4 * g + 0], v[4 * g + 1]), pack_bf16x2(v[4 * g + 2], v[4 * g + 3]));
-        const int slot = (d0 >> 3) ^ (erow & 15);
-        *reinterpret_cast<lds_u32x2*>(eb + erow * 128 + slot * 8 + 4 * hf) = u32x2_t{w.x, w.y};
       }
+      const uint2 w = make_uint2(pack_bf16x2(v[4 * g + 0], v[4 * g + 1]), pack_bf16x2(v[4 * g + 2], v[4 * g + 3]));
+      const int slot = (d0 >> 3) ^ (erow & 15);
+      *reinterpret_cast<lds_u32x2*>(eb + erow * 128 + slot * 8 + 4 * hf) = u32x2_t{w.x, w.y};
     }
   }
   // row segments out: instruction j covers token rows 4 j .. 4 j + 3, lane l the 16-byte chunk l & 15
