@@ -313,8 +313,9 @@ __global__ __launch_bounds__(kThreads, kQB == 1 ? 2 : 1) void attn_fwd_kernel(Fw
     return __builtin_bit_cast(bf16x8_t, both);
   };
   // O^T += V^T P^T over the tile's 16-key chunks and four 32-dim blocks of V buffer `buf`; the
-  // operands of the first kVPre chunks may have been read already (pre)
-  constexpr int kVPre = 2;
+  // operands of the first kVPre chunks may have been read already (pre).  The lagging waves read
+  // all of them while they wait at the barrier.
+  constexpr int kVPre = 2 * kKB;
   auto pv_pre = [&](int buf, const bf16x8_t (&pb)[kQB][kKB][2], const bf16x8_t (&pre)[kVPre][4], auto use_pre) {
 #pragma unroll
     for (int kc = 0; kc < 2 * kKB; ++kc)
@@ -442,8 +443,8 @@ __global__ __launch_bounds__(kThreads, kQB == 1 ? 2 : 1) void attn_fwd_kernel(Fw
       store_tile((t_begin + 1) % kNBuf);
       for (int t = t_begin + 1; t + 1 < t_end; ++t) {
         // V of tile t - 1 has been visible since barrier t - 1.  Barrier t is taken in two
-        // halves (release, then wait and acquire) so that the first PV operands are read while
-        // this wave waits for the others.
+        // halves (release, then wait and acquire) so that the PV operands are read while this
+        // wave waits for the others.
         bf16x8_t pre[kVPre][4];
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
 #pragma unroll
