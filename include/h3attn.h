@@ -225,9 +225,10 @@ int h3attn_adaln_residual(const void* x, const void* y, int64_t xy_stride, const
  * Device call.  y = x W^T (+ bias), then, for the leading rope_cols output
  * features (whole 128-wide heads), the rotation of h3attn_rope_qk applied to the
  * float32 results with each row's (cos, sin) from a table made by
- * h3attn_rope_table, then one rounding to bf16 (nearest even).  For the fused QKV projection of H heads: W is [3 H 128][k] (Q rows,
- * then K, then V), rope_cols = 2 H 128, and y = [m][3][H][128] feeds
- * h3attn_forward with rope_q = 0 through strided views (row stride 3 H 128).
+ * h3attn_rope_table, then one rounding to bf16 (nearest even).  For the fused
+ * QKV projection of H heads: W is [3 H 128][k] (Q rows, then K, then V),
+ * rope_cols = 2 H 128, and y = [m][3][H][128] feeds h3attn_forward with
+ * rope_q = 0 through strided views (row stride 3 H 128).
  * Readings: no bias unless given; W is stored [n_out][k] (row = output feature).
  *   x          bf16 [m][x_stride], w bf16 [n_out][w_stride], bias bf16 [n_out] or NULL
  *   y          out: bf16 [m][y_stride]; must not overlap x, w or bias
@@ -239,7 +240,8 @@ int h3attn_adaln_residual(const void* x, const void* y, int64_t xy_stride, const
  * Strides are in elements, multiples of 8 (x, w >= k; y >= n_out); pointers
  * 16-byte aligned.  Arithmetic: float32 accumulation of exact bf16 products.
  * m == 0 is a no-op.  Errors: EINVAL, ERANGE (m >= 2^31, 256 rows of x, w or y
- * spanning 2^31 bytes, x spanning 2^32 bytes), EUNSUPPORTED, EHIP.
+ * spanning 2^31 bytes, x spanning 2^32 bytes, 2^30 or more 256 x 256 tiles),
+ * EUNSUPPORTED, EHIP.
  */
 #define H3ATTN_LINEAR_TILE 256
 #define H3ATTN_LINEAR_KSTEP 64
