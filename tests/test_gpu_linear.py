@@ -195,3 +195,28 @@ def test_rope_table_matches_oracle(gpu_lib, cfg_name):
     err = np.abs(got[:n] - ref)
     print("%s table max|err| %.3e" % (cfg_name, float(err.max())), flush=True)
     assert err.max() <= 2.5e-7
+
+
+@pytest.mark.parametrize("sections,thetas", [((48, 40, 40), (5.0e5, 1.0e4, 2.0e3)), ((128, 0, 0), (1.0e4, 1.0e4, 1.0e4))])
+def test_rope_table_other_configs(gpu_lib, sections, thetas):
+    """The table and the projection that reads it follow the configuration passed to h3attn_rope_table
+    (section split and per-axis bases), not the default one; same bounds as above."""
+    h3 = gpu_lib
+    m, heads, k = 300, 2, 256
+    n = 3 * heads * 128
+    x, w, b = W.projection_inputs(m, k, n, seed=77)
+    coords_h = h3.build_coords(segs_of(m))
+    coords = torch.from_numpy(coords_h).cuda()
+    table = torch.empty((m, 64, 2), dtype=torch.float32, device="cuda")
+    h3.rope_table(h3.rope_cfg(sections, thetas), coords, m, table)
+    yd = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    h3.linear(dev_bf16(x), k, dev_bf16(w), k, dev_bf16(b), yd, n, m, n, k, table, 2 * heads * 128)
+    torch.cuda.synchronize()
+    unit = np.zeros((m, 1, 128))
+    unit[:, :, 0::2] = 1.0
+    ref_tab = oracle.rope(unit, coords_h, sections, thetas)[:, 0].reshape(m, 64, 2)
+    terr = np.abs(table.cpu().numpy().astype(np.float64) - ref_tab).max()
+    print("sections %s table max|err| %.3e" % (sections, terr), flush=True)
+    assert terr <= 2.5e-7
+    ref = qkv_rope(f64(x), f64(w), f64(b), coords_h, heads, sections, thetas)
+    check(host_bits(yd), ref, f64(x), f64(w), f64(b), 2 * heads * 128, "qkv sections %s" % (sections,))
