@@ -235,9 +235,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs a) {
   const int yrow_bytes = static_cast<int>(a.y_stride * 2);
   const __amdgpu_buffer_rsrc_t yd = __builtin_amdgcn_make_buffer_rsrc(
       a.y + int64_t(tw0) * a.y_stride + fw0, 0, rows > 0 ? (rows - 1) * yrow_bytes + 256 : 0, kRsrcFlags);
+  const bool table = rotate && rows > 0;               // a NULL table (no rotation) is never offset
   const __amdgpu_buffer_rsrc_t td = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(a.rope_tab) + int64_t(tw0) * (2 * kPairs), 0, rotate && rows > 0 ? rows * kPairs * 8 : 0,
-      kRsrcFlags);
+      table ? const_cast<float*>(a.rope_tab) + int64_t(tw0) * (2 * kPairs) : reinterpret_cast<float*>(a.y), 0,
+      table ? rows * kPairs * 8 : 0, kRsrcFlags);
   // (cos, sin) of the lane's pairs fb 16 + 4 g + 2 hf and the next one, token block tb: 16 bytes
   auto rot4 = [&](int tb, int fb, int g) {
     return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
