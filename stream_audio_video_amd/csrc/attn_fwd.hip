@@ -407,10 +407,10 @@ __global__ __launch_bounds__(kThreads, kQB == 1 ? 2 : 1) void attn_fwd_kernel(Fw
   // matrix pipe and then both leaving it idle: the leading half (waves 0 .. kWaves/2 - 1) runs
   // scores, softmax and PV of tile t after barrier t; the lagging half runs PV of tile t - 1 and
   // then scores and softmax of tile t, keeping P in registers across the barrier.  The lagging
-  // half still reads V of tile t - 1 after barrier t, hence the third buffer; it reads the first
-  // of those operands while it waits at the barrier.  Each wave's own
-  // arithmetic is the same in both halves, so the result does not depend on the half.  The last
-  // step masks keys >= n, which only bites on the sequence's last tile.
+  // half issues its reads of V of tile t - 1 while it waits at barrier t and they may complete
+  // after it, hence the third buffer.  Each wave's own arithmetic is the same in both halves, so
+  // the result does not depend on the half.  The last step masks keys >= n, which only bites on
+  // the sequence's last tile.
   load_tile(t_begin);
   store_tile(t_begin % kNBuf);
   __syncthreads();
