@@ -162,6 +162,14 @@ def matched_check(h3, segs, q, k, v, tag, heads=None, workers=4):
     kt = A.round_bf16(oracle.rope(f64(k[:, heads]), c, SEC, TH))
     qt_bits, kt_bits = np.zeros(q.shape, np.uint16), np.zeros(k.shape, np.uint16)
     qt_bits[:, heads], kt_bits[:, heads] = A.bits_of_bf16(qt), A.bits_of_bf16(kt)
+    return matched_compare(h3, qt_bits, kt_bits, v, c, tag, heads, workers)
+
+
+def matched_compare(h3, qt_bits, kt_bits, v, c, tag, heads, workers=4):
+    """The comparison of matched_check on given pre-rotated bf16 Q~ and K~ (bits [N, H, 128]);
+    only the heads in `heads` are compared, and c only gives the row count to the oracle."""
+    n, h = qt_bits.shape[0], qt_bits.shape[1]
+    qt, kt = f64(qt_bits[:, heads]), f64(kt_bits[:, heads])
     scale = np.float32(1.0 / np.sqrt(128.0))
     qhat = A.round_bf16((qt.astype(np.float32) * prescale32(scale)).astype(np.float64))
     o_bits, lse = run_prerotated(h3, qt_bits, kt_bits, v, n, h, scale)
@@ -347,6 +355,61 @@ def test_forward_very_peaky_rows(gpu_lib, n):
     # a row whose weight moves between two keys changes by at most their difference
     assert mx <= 2.0 * vmax and rel <= 0.08 and le <= 0.5
     matched_check(h3, segs, q, k, v, "very peaky n=%d" % nn)
+
+
+def hadamard(n):
+    """Sylvester's +-1 matrix of order n (a power of two): rows mutually orthogonal."""
+    h = np.ones((1, 1))
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def test_forward_tile_signatures(gpu_lib):
+    """A detector for races on the K/V tile buffers in LDS (a tile read before it is stored,
+    after it is overwritten, or from the wrong buffer).  Random inputs hide such a fault at
+    long sequences, where one tile of hundreds moves an output by well under the tolerance;
+    here every 64-key tile is made conspicuous.  Q~ and K~ are given pre-rotated:
+      * every key of tile j carries row j of a 128 x 128 Hadamard matrix (times 1/8), so the
+        101 tiles have mutually orthogonal keys and each score is exactly 0 or S;
+      * query q picks a target tile, (37 q + 11 h) mod 101, and carries that tile's row, so its
+        scores are S on its target tile and exactly 0 elsewhere;
+      * the values of tile j are a pattern of its own (multiples of 1/16, exact in bf16).
+    Heads 0 and 2 use S = 2 in log2 units: every key keeps weight, a lane's tile sum stays at
+    128, the fast path runs, and the target tile holds 4 % of a row's weight, so a wrong V tile
+    anywhere moves every row, and a wrong K tile moves the rows that target it, by hundreds of
+    times the bound below.  Heads 1 and 3 use S = 24: each row's weight sits on its target tile,
+    every wave takes the slow path that raises the reference on the tiles its rows target, and
+    O is the target tile's mean value row.  Each workgroup's 256 rows target every tile two or
+    three times, so every (workgroup, tile) pair is watched, on both paths.  Expected values: the
+    matched-input oracle comparison (module text)."""
+    h3 = gpu_lib
+    n, heads = 64 * 100 + 37, 4
+    nt = (n + 63) // 64
+    had = hadamard(128)
+    tile = np.arange(n) // 64
+    pre = float(prescale32(np.float32(1.0 / np.sqrt(128.0))))
+    a = 0.125
+    rng = np.random.default_rng(2024)
+    qt = np.zeros((n, heads, 128))
+    kt = np.zeros((n, heads, 128))
+    v = np.zeros((n, heads, 128))
+    jitter = ((np.arange(n)[:, None] * 13 + np.arange(128)[None, :]) % 7 - 3) / 16.0
+    for hd in range(heads):
+        sig = (np.arange(128) * 5 + 7 * hd) % 128           # a per-head permutation of the rows
+        kt[:, hd] = a * had[sig[tile]]
+        target = (np.arange(n) * 37 + 11 * hd) % nt
+        s_log2 = 2.0 if hd % 2 == 0 else 24.0
+        b = A.round_bf16(np.array(s_log2 / (128.0 * a * pre)))
+        qt[:, hd] = b * had[sig[target]]
+        base = rng.choice([-1.5, -1.0, -0.5, 0.5, 1.0, 1.5], size=(nt, 128))
+        v[:, hd] = base[tile] + jitter
+    assert np.array_equal(A.round_bf16(qt), qt) and np.array_equal(A.round_bf16(v), v)
+    segs = [W.text(n, 0)]
+    c = oracle.build_coords(segs)
+    ro, rl = matched_compare(h3, A.bits_of_bf16(qt), A.bits_of_bf16(kt), A.bits_of_bf16(v), c, "signatures",
+                             list(range(heads)))
+    print("tile signatures: worst O error %.2f, LSE %.2f of the bound" % (ro, rl), flush=True)
 
 
 def test_forward_strided_views(gpu_lib):
