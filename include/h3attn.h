@@ -325,10 +325,11 @@ int h3attn_av_euler_pack(float* video_latent, int32_t channels, int32_t frames, 
  * and the row's max / sum) in the workspace, merged by a second kernel with the
  * same max-and-rescale rule.  A cost model of that last stretch (the waves of
  * parts it takes, plus the merge's traffic) picks the number of parts, 2 to 8,
- * and splits only when that saves at least a tenth of a unit's time.  The result equals h3attn_forward
- * up to the rounding order of the split rows.  A NULL or too small workspace
- * runs the unsplit schedule (h3attn_forward); the library still allocates
- * nothing.  The workspace must not be shared by calls in flight at once.
+ * and splits only when that saves at least a tenth of a unit's time.  The
+ * result equals h3attn_forward up to the rounding order of the split rows.  A
+ * NULL or too small workspace runs the unsplit schedule (h3attn_forward); the
+ * library still allocates nothing.  The workspace must not be shared by calls
+ * in flight at once.
  */
 int h3attn_forward_ws(const h3attn_rope_cfg* cfg, const float* coords_dev, int32_t rope_q,
                       const void* q, const void* k, const void* v, void* o, float* lse,
