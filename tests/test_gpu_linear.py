@@ -136,7 +136,9 @@ def test_rows_past_m_untouched(gpu_lib, rope):
 
 
 def test_full_size_qkv_sampled(gpu_lib):
-    """The 5 s fused QKV projection (28,192 x 5,376 -> 16,128) in the benchmark's launch shape; sampled rows."""
+    """The 5 s fused QKV projection (28,192 x 5,376 -> 16,128) in the benchmark's launch shape:
+    sampled rows over all 16,128 features, then every row of the Q, K and V slabs of heads 0 and
+    41 (the first and last feature tiles of each part, and the last, 32-row token tile)."""
     _, segs = W.CONFIGS["5s"]
     m, k, heads = W.n_tokens(segs), W.ADALN_HIDDEN, 42
     n = 3 * heads * 128
@@ -147,6 +149,31 @@ def test_full_size_qkv_sampled(gpu_lib):
     ref = qkv_rope(f64(x[rows]), f64(w), f64(b), coords_h[rows], heads, SEC, TH)
     check(y[rows], ref, f64(x[rows]), f64(w), f64(b), 2 * heads * 128, "5s qkv")
     assert not np.any((y & np.uint16(0x7F80)) == np.uint16(0x7F80))      # no bf16 inf / NaN anywhere
+    xs = f64(x)
+    for h in (0, heads - 1):
+        # the one-head fused projection of head h: its Q, K and V weight rows, rotated as in the
+        # full projection (the rotation acts on each head alone)
+        cols = np.concatenate([np.arange(p * heads * 128 + h * 128, p * heads * 128 + (h + 1) * 128)
+                               for p in range(3)])
+        ws, bs = f64(w[cols]), f64(b[cols])
+        ref = qkv_rope(xs, ws, bs, coords_h, 1, SEC, TH)
+        check(y[:, cols], ref, xs, ws, bs, 256, "5s qkv head %d, all rows" % h)
+
+
+def test_full_size_output_projection(gpu_lib):
+    """The 5 s output projection (28,192 x 5,376 -> 5,376, no rotation) in the block's launch shape:
+    every row of the first and last 256-feature tiles, and sampled rows over all features."""
+    _, segs = W.CONFIGS["5s"]
+    m, k = W.n_tokens(segs), W.ADALN_HIDDEN
+    n = k
+    x, w, b = W.projection_inputs(m, k, n, seed=W.DEFAULT_SEED + 40)
+    y = run(gpu_lib, x, w, b, m, n, k)
+    xs = f64(x)
+    cols = np.r_[0:256, n - 256:n]
+    check(y[:, cols], linear(xs, f64(w[cols]), f64(b[cols])), xs, f64(w[cols]), f64(b[cols]), 0,
+          "5s out-proj, edge feature tiles, all rows")
+    rows = np.unique(np.r_[0, m - 1, np.random.default_rng(9).integers(0, m, 16)])
+    check(y[rows], linear(xs[rows], f64(w), f64(b)), xs[rows], f64(w), f64(b), 0, "5s out-proj, sampled rows")
 
 
 def test_projection_feeds_attention(gpu_lib):
